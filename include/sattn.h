@@ -1,0 +1,191 @@
+/*
+ * sattn.h — C ABI of the MI355X (gfx950) quantized video-DiT self-attention library.
+ *
+ * The numerical program follows the pages "h3-blackwell-runtime/PERFORMANCE_ROADMAP.md"
+ * (sections "Measured GB10 Baseline" → "SageAttention 2.2.0 internals", the Sage2 phase
+ * decomposition paragraph after "The fresh block kernel-time distribution", and "Phase 4:
+ * Dense Sage-Compatible Attention") and "research/vortex_exact_attention/
+ * PHASE2B_ALIGNED_REPORT.md" (sections "Decision" and "Exactness"):
+ *
+ *   1. K smoothing: subtract the per-(sequence, head, channel) mean of K.
+ *   2. Q and smoothed K → symmetric INT8, one FP32 scale per 64-token block.
+ *   3. V → OCP FP8 E4M3, one FP32 scale per (sequence, head, channel).
+ *   4. Scores: INT8·INT8 → exact INT32 accumulators → FP32 scores.
+ *   5. Online softmax over 64-key epochs in increasing key order (running max m and
+ *      denominator d per query row), probabilities → E4M3 (×448), FP8 P·V with FP32
+ *      accumulation into the running output RO, final reciprocal of d, BF16 output.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library never
+ *    allocates device memory and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
+ *    entry point only enqueues work on `stream`; nothing synchronises the host.
+ *  - Argument validation is synchronous and happens before any HIP call: a call that
+ *    returns anything but SATTN_OK has enqueued nothing.  A failed kernel launch is
+ *    reported as SATTN_EHIP.  Device-side faults surface at the caller's next
+ *    synchronisation.  No C++ exception crosses this interface.
+ *  - Head dimension D must be 128.
+ *  - BF16 views: element (b, t, h, c) lives at ptr + b*stride_b + t*stride_t + h*stride_h + c
+ *    (strides in elements; the channel stride is 1).  The base pointer must be 16-byte
+ *    aligned and stride_t, stride_h, stride_b multiples of 8, so every (token, head) row
+ *    is 256 contiguous, 16-byte-aligned bytes.  This admits contiguous BLHD/BHLD tensors
+ *    and the projection-strided slices of a fused [L, 3, H, D] QKV tensor.
+ *  - Sequences ("segments"): in dense mode there are B segments of Lq query tokens and
+ *    Lk key tokens each (segment b uses batch index b).  In varlen mode the segments are
+ *    given by device int32 prefix sums cu_seqlens_q / cu_seqlens_k of length nseg+1
+ *    (cu[0] = 0, non-decreasing); segment s covers packed tokens [cu[s], cu[s+1]) and
+ *    stride_b is ignored.  Attention is block-diagonal: each segment's queries attend
+ *    to its own keys only, with no causal mask.  Empty segments are legal.
+ *
+ * Quantized buffers (written by sattn_quantize_qkv, read by sattn_fwd*)
+ * ---------------------------------------------------------------------
+ *  Each segment's tokens are padded to whole 64-token blocks.  Segment s starts at
+ *  block index  s*ceil(Lq/64)  (dense)  or  cu[s]/64 + s  (varlen, integer division).
+ *  Capacities in blocks:  qblk_cap >= floor(total_q/64) + nseg  (likewise kblk_cap),
+ *  where total_q is B*Lq (dense) or cu_seqlens_q[nseg] (varlen); sattn_quant_query
+ *  returns exactly that bound.  Padding rows are written as zeros.
+ *
+ *  q, k : int8,  [H][blk_cap][8192]: one 8 KiB tile per 64-token block in MFMA operand
+ *         order.  Byte ((t*4 + u)*64 + g*32 + i)*16 + s of a tile holds token 32*t + i,
+ *         channel 64*g + 16*u + s (t,g in {0,1}; u in 0..3; i in 0..31; s in 0..15).
+ *  q_scale, k_scale : float, [H][blk_cap], the FP32 scale of each 64-token block.
+ *  k_mean : float, [nseg][H][128], the per-channel mean subtracted from K.
+ *  v    : OCP E4M3 bytes, [H][kblk_cap][8192]: one tile per 64-key block, channel-major.
+ *         Byte ((w*2 + f)*64 + g*32 + i)*16 + s holds channel 32*w + i and key
+ *         32*f + 8*(s/4) + 4*g + (s%4) of the block (w in 0..3; f,g in {0,1}).
+ *  v_scale : float, [nseg][H][128], the per-channel FP32 scale of V.
+ */
+#ifndef SATTN_H_
+#define SATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sattn_status;
+#define SATTN_OK 0
+#define SATTN_EINVAL 1       /* bad pointer, size, stride, alignment or segment count   */
+#define SATTN_EUNSUPPORTED 2 /* well-formed but outside what the kernels implement (D)  */
+#define SATTN_ENOSPACE 3     /* a capacity or workspace is smaller than required       */
+#define SATTN_EHIP 4         /* a HIP launch or runtime call failed                    */
+
+/* Strided BF16 input view (see the conventions above). */
+typedef struct {
+  const void* ptr;
+  int64_t stride_b, stride_t, stride_h;
+} sattn_bf16_in;
+
+/* Strided BF16 output view: same addressing as the input, token-major. */
+typedef struct {
+  void* ptr;
+  int64_t stride_b, stride_t, stride_h;
+} sattn_bf16_out;
+
+/* Caller-owned quantized Q/K/V buffers and their capacities (see the layout above). */
+typedef struct {
+  int8_t* q;
+  float* q_scale;
+  int8_t* k;
+  float* k_scale;
+  float* k_mean;
+  uint8_t* v;
+  float* v_scale;
+  int64_t qblk_cap, kblk_cap;
+} sattn_qkv_quant;
+
+/* Byte sizes of every buffer of sattn_qkv_quant, plus scratch sizes. */
+typedef struct {
+  int64_t qblk_cap, kblk_cap;
+  size_t q_bytes, q_scale_bytes, k_bytes, k_scale_bytes, k_mean_bytes, v_bytes, v_scale_bytes;
+  size_t quant_workspace_bytes; /* workspace of sattn_quantize_qkv                     */
+  size_t fwd_workspace_bytes;   /* workspace of sattn_fwd_varlen (0 is enough for dense) */
+} sattn_sizes;
+
+/*
+ * sattn_quant_query — host-only, pure.  Fills *out for nseg segments holding total_q
+ * query tokens and total_k key tokens (dense: nseg = B, total = B*L) with H heads and
+ * head dimension D.  Returns SATTN_EINVAL for nseg < 1, negative totals, H < 1 or a null
+ * `out`, and SATTN_EUNSUPPORTED for D != 128.
+ */
+sattn_status sattn_quant_query(int nseg, int64_t total_q, int64_t total_k, int H, int D, sattn_sizes* out);
+
+/*
+ * sattn_quantize_qkv — steps 1–3 of the program above ("Q/K INT8 quantization", "V FP8
+ * quantization" and "K smoothing" in the SageAttention internals table of the roadmap
+ * page; the later decomposition into K smoothing, Q/K quantization and V
+ * transpose/quantization phases).
+ *
+ *   dense  (cu_seqlens_q == cu_seqlens_k == NULL): nseg = B segments; q holds B x Lq
+ *          tokens, k and v hold B x Lk tokens.
+ *   varlen (both non-NULL): device int32 arrays of nseg+1 entries; Lq and Lk are the
+ *          number of packed tokens the q and k/v views hold (cu[nseg] must not exceed
+ *          them; tokens beyond are never read, and a segment reaching past them is
+ *          clipped on the device).
+ *
+ * For each segment s, head h, channel c (all sums in FP64, every scale operation a single
+ * correctly rounded FP32 operation):
+ *   k_mean[s,h,c] = fl32( (sum_t K[t,h,c]) / Lk_s ),  K' = fl32(K - k_mean)
+ *   per 64-token block: amax = max|x|, scale = fl32(amax/127), inv = fl32(127/amax),
+ *     code = clamp(rne(fl32(x*inv)), -127, 127)   (x = Q, or K'; amax = 0 → scale 0, codes 0)
+ *   v_scale[s,h,c] = fl32(amax_V/448), V8 = e4m3_rne(fl32(V * fl32(448/amax_V)))
+ *
+ * `workspace` must hold quant_workspace_bytes from sattn_quant_query (16-byte aligned);
+ * it is scratch: its contents are undefined after the call.  Returns SATTN_ENOSPACE when
+ * a capacity in `out` or workspace_bytes is too small.
+ */
+sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in v, int nseg, int H, int D,
+                                int64_t Lq, int64_t Lk, const int32_t* cu_seqlens_q,
+                                const int32_t* cu_seqlens_k, const sattn_qkv_quant* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
+ * sattn_fwd — dense attention forward over quantized inputs (steps 4–5; the pages'
+ * "Attention forward" / prequantized mainloop, and the checkpoint list of the
+ * Phase 2B report's "Exactness" section).  B segments of Lq queries and Lk keys, H heads,
+ * D = 128.  sm_scale multiplies q·k (usually 1/sqrt(D)); it must be finite and > 0.
+ * The score of query i and key j in 64-blocks (bq, bk) is
+ *   S = fl32(acc * sigma),  sigma = fl32(fl32(q_scale[bq] * c) * k_scale[bk]),
+ *   c = fl32(sm_scale * log2(e)) computed in double on the host,
+ * and the softmax runs in base 2.  o receives BF16 rows for every valid query token
+ * (rows of padding are not written).  A segment with Lq > 0 and Lk = 0 writes zeros.
+ */
+sattn_status sattn_fwd(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D, float sm_scale,
+                       sattn_bf16_out o, void* stream);
+
+/*
+ * sattn_fwd_varlen — block-diagonal (per-segment) version of sattn_fwd for packed
+ * sequences; cu_seqlens_q/k are the same device arrays given to sattn_quantize_qkv.
+ * total_q is the number of packed query tokens the output view holds (rows past it are
+ * never written).  `workspace` (fwd_workspace_bytes, 16-byte aligned) receives the
+ * longest-first schedule of the segments and is scratch for the caller.
+ */
+sattn_status sattn_fwd_varlen(const sattn_qkv_quant* qkv, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int nseg, int64_t total_q, int H, int D,
+                              float sm_scale, sattn_bf16_out o, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * sattn_debug_scores — checkpoint dump for one (segment, head) of a dense problem
+ * (the Phase 2B report's "INT32-to-FP32 QK scores" checkpoint).  Runs the same
+ * forward kernel as sattn_fwd with a dump enabled and writes, for every query row
+ * i < Lq and key j < Lk of segment `seg`, head `head`:
+ *   acc_out[i*Lk + j] = the exact INT32 accumulator, s_out[i*Lk + j] = fl32(acc*sigma).
+ * Both buffers are device memory of Lq*Lk elements.  The forward output is written to
+ * `o` exactly as sattn_fwd would for that (segment, head).
+ */
+sattn_status sattn_debug_scores(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D,
+                                float sm_scale, int seg, int head, int32_t* acc_out, float* s_out,
+                                sattn_bf16_out o, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* sattn_status_string(sattn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SATTN_H_ */
