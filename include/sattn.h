@@ -66,6 +66,12 @@
 extern "C" {
 #endif
 
+#if defined(__GNUC__)
+#define SATTN_API __attribute__((visibility("default")))
+#else
+#define SATTN_API
+#endif
+
 typedef int32_t sattn_status;
 #define SATTN_OK 0
 #define SATTN_EINVAL 1       /* bad pointer, size, stride, alignment or segment count   */
@@ -111,7 +117,7 @@ typedef struct {
  * head dimension D.  Returns SATTN_EINVAL for nseg < 1, negative totals, H < 1 or a null
  * `out`, and SATTN_EUNSUPPORTED for D != 128.
  */
-sattn_status sattn_quant_query(int nseg, int64_t total_q, int64_t total_k, int H, int D, sattn_sizes* out);
+SATTN_API sattn_status sattn_quant_query(int nseg, int64_t total_q, int64_t total_k, int H, int D, sattn_sizes* out);
 
 /*
  * sattn_quantize_qkv — steps 1–3 of the program above ("Q/K INT8 quantization", "V FP8
@@ -137,7 +143,7 @@ sattn_status sattn_quant_query(int nseg, int64_t total_q, int64_t total_k, int H
  * it is scratch: its contents are undefined after the call.  Returns SATTN_ENOSPACE when
  * a capacity in `out` or workspace_bytes is too small.
  */
-sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in v, int nseg, int H, int D,
+SATTN_API sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in v, int nseg, int H, int D,
                                 int64_t Lq, int64_t Lk, const int32_t* cu_seqlens_q,
                                 const int32_t* cu_seqlens_k, const sattn_qkv_quant* out, void* workspace,
                                 size_t workspace_bytes, void* stream);
@@ -153,7 +159,7 @@ sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in 
  * and the softmax runs in base 2.  o receives BF16 rows for every valid query token
  * (rows of padding are not written).  A segment with Lq > 0 and Lk = 0 writes zeros.
  */
-sattn_status sattn_fwd(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D, float sm_scale,
+SATTN_API sattn_status sattn_fwd(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D, float sm_scale,
                        sattn_bf16_out o, void* stream);
 
 /*
@@ -163,7 +169,7 @@ sattn_status sattn_fwd(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk,
  * never written).  `workspace` (fwd_workspace_bytes, 16-byte aligned) receives the
  * longest-first schedule of the segments and is scratch for the caller.
  */
-sattn_status sattn_fwd_varlen(const sattn_qkv_quant* qkv, const int32_t* cu_seqlens_q,
+SATTN_API sattn_status sattn_fwd_varlen(const sattn_qkv_quant* qkv, const int32_t* cu_seqlens_q,
                               const int32_t* cu_seqlens_k, int nseg, int64_t total_q, int H, int D,
                               float sm_scale, sattn_bf16_out o, void* workspace, size_t workspace_bytes,
                               void* stream);
@@ -177,12 +183,12 @@ sattn_status sattn_fwd_varlen(const sattn_qkv_quant* qkv, const int32_t* cu_seql
  * Both buffers are device memory of Lq*Lk elements.  The forward output is written to
  * `o` exactly as sattn_fwd would for that (segment, head).
  */
-sattn_status sattn_debug_scores(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D,
+SATTN_API sattn_status sattn_debug_scores(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D,
                                 float sm_scale, int seg, int head, int32_t* acc_out, float* s_out,
                                 sattn_bf16_out o, void* stream);
 
 /* Static, human-readable name of a status code. */
-const char* sattn_status_string(sattn_status s);
+SATTN_API const char* sattn_status_string(sattn_status s);
 
 #ifdef __cplusplus
 }

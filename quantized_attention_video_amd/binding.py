@@ -1,0 +1,239 @@
+"""ctypes binding of libsattn.so (include/sattn.h) — argument marshalling only.
+
+Every function here has the name of the C entry point it wraps.  torch tensors supply
+device memory and the current HIP stream; all computation happens in the library's
+kernels.  If the library has not been built the calls raise; there is no fallback.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsattn.so")
+D = 128
+
+SATTN_OK, SATTN_EINVAL, SATTN_EUNSUPPORTED, SATTN_ENOSPACE, SATTN_EHIP = range(5)
+EXPORTED = ("sattn_quant_query", "sattn_quantize_qkv", "sattn_fwd", "sattn_fwd_varlen", "sattn_debug_scores",
+            "sattn_status_string")
+
+
+class SattnError(RuntimeError):
+    def __init__(self, status, name):
+        super().__init__(f"{name} failed: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class BF16In(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("stride_b", ctypes.c_int64), ("stride_t", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64)]
+
+
+class BF16Out(ctypes.Structure):
+    _fields_ = BF16In._fields_
+
+
+class QKVQuant(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("q_scale", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("k_mean", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("qblk_cap", ctypes.c_int64), ("kblk_cap", ctypes.c_int64)]
+
+
+class Sizes(ctypes.Structure):
+    _fields_ = [("qblk_cap", ctypes.c_int64), ("kblk_cap", ctypes.c_int64), ("q_bytes", ctypes.c_size_t),
+                ("q_scale_bytes", ctypes.c_size_t), ("k_bytes", ctypes.c_size_t),
+                ("k_scale_bytes", ctypes.c_size_t), ("k_mean_bytes", ctypes.c_size_t),
+                ("v_bytes", ctypes.c_size_t), ("v_scale_bytes", ctypes.c_size_t),
+                ("quant_workspace_bytes", ctypes.c_size_t), ("fwd_workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m quantized_attention_video_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, vp, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+        L.sattn_quant_query.argtypes = [i32, i64, i64, i32, i32, ctypes.POINTER(Sizes)]
+        L.sattn_quantize_qkv.argtypes = [BF16In, BF16In, BF16In, i32, i32, i32, i64, i64, vp, vp,
+                                         ctypes.POINTER(QKVQuant), vp, ctypes.c_size_t, vp]
+        L.sattn_fwd.argtypes = [ctypes.POINTER(QKVQuant), i32, i32, i32, i32, i32, f32, BF16Out, vp]
+        L.sattn_fwd_varlen.argtypes = [ctypes.POINTER(QKVQuant), vp, vp, i32, i64, i32, i32, f32, BF16Out, vp,
+                                       ctypes.c_size_t, vp]
+        L.sattn_debug_scores.argtypes = [ctypes.POINTER(QKVQuant), i32, i32, i32, i32, i32, f32, i32, i32, vp, vp,
+                                         BF16Out, vp]
+        L.sattn_status_string.argtypes = [i32]
+        L.sattn_status_string.restype = ctypes.c_char_p
+        for name in EXPORTED[:-1]:
+            getattr(L, name).restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().sattn_status_string(int(status)).decode()
+
+
+def _check(status, name):
+    if status != SATTN_OK:
+        raise SattnError(status, name)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _view(t, cls):
+    """A [B, L, H, D] or [T, H, D] BF16 tensor view → its C struct (strides in elements)."""
+    if t.dtype != torch.bfloat16 or t.shape[-1] != D or t.stride(-1) != 1:
+        raise ValueError("expected a bfloat16 view with a contiguous last dimension of 128")
+    if t.dim() == 4:
+        return cls(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+    if t.dim() == 3:
+        return cls(t.data_ptr(), 0, t.stride(0), t.stride(1))
+    raise ValueError("expected a 3-d [T, H, D] or 4-d [B, L, H, D] view")
+
+
+def sattn_quant_query(nseg, total_q, total_k, H, D_=D):
+    s = Sizes()
+    _check(lib().sattn_quant_query(nseg, total_q, total_k, H, D_, ctypes.byref(s)), "sattn_quant_query")
+    return s
+
+
+@dataclass
+class Quantized:
+    """Device buffers of sattn_qkv_quant plus the quantization workspace."""
+    q: torch.Tensor
+    q_scale: torch.Tensor
+    k: torch.Tensor
+    k_scale: torch.Tensor
+    k_mean: torch.Tensor
+    v: torch.Tensor
+    v_scale: torch.Tensor
+    workspace: torch.Tensor
+    qblk_cap: int
+    kblk_cap: int
+    nseg: int
+    H: int
+    sizes: Sizes
+
+    def struct(self):
+        return QKVQuant(self.q.data_ptr(), self.q_scale.data_ptr(), self.k.data_ptr(), self.k_scale.data_ptr(),
+                        self.k_mean.data_ptr(), self.v.data_ptr(), self.v_scale.data_ptr(), self.qblk_cap,
+                        self.kblk_cap)
+
+
+def alloc_quantized(nseg, total_q, total_k, H, device="cuda"):
+    """Allocate (uninitialised) quantized buffers sized by sattn_quant_query."""
+    s = sattn_quant_query(nseg, total_q, total_k, H)
+    e = dict(device=device)
+    return Quantized(
+        q=torch.empty((H, s.qblk_cap, 8192), dtype=torch.int8, **e),
+        q_scale=torch.empty((H, s.qblk_cap), dtype=torch.float32, **e),
+        k=torch.empty((H, s.kblk_cap, 8192), dtype=torch.int8, **e),
+        k_scale=torch.empty((H, s.kblk_cap), dtype=torch.float32, **e),
+        k_mean=torch.empty((nseg, H, D), dtype=torch.float32, **e),
+        v=torch.empty((H, s.kblk_cap, 8192), dtype=torch.uint8, **e),
+        v_scale=torch.empty((nseg, H, D), dtype=torch.float32, **e),
+        workspace=torch.empty(max(s.quant_workspace_bytes, 16), dtype=torch.uint8, **e),
+        qblk_cap=s.qblk_cap, kblk_cap=s.kblk_cap, nseg=nseg, H=H, sizes=s)
+
+
+def sattn_quantize_qkv(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, out=None, stream=None):
+    """Quantize BF16 Q/K/V views.  Dense: [B, L, H, D] views.  Varlen: packed [T, H, D]
+    views plus device int32 cu_seqlens tensors of nseg+1 entries."""
+    varlen = cu_seqlens_q is not None
+    if varlen:
+        nseg = cu_seqlens_q.numel() - 1
+        H = q.shape[1]
+        Lq, Lk = q.shape[0], k.shape[0]
+        total_q, total_k = Lq, Lk
+    else:
+        nseg, Lq, H = q.shape[0], q.shape[1], q.shape[2]
+        Lk = k.shape[1]
+        total_q, total_k = nseg * Lq, nseg * Lk
+    if out is None:
+        out = alloc_quantized(nseg, total_q, total_k, H, device=q.device)
+    st = out.struct()
+    _check(lib().sattn_quantize_qkv(_view(q, BF16In), _view(k, BF16In), _view(v, BF16In), nseg, H, D, Lq, Lk,
+                                    _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), ctypes.byref(st),
+                                    out.workspace.data_ptr(), out.workspace.numel(), _stream(stream)),
+           "sattn_quantize_qkv")
+    return out
+
+
+def sattn_fwd(quant, B, H, Lq, Lk, sm_scale, out=None, stream=None):
+    """Dense forward; returns (or fills) a BF16 [B, Lq, H, D] tensor (any strided view works)."""
+    if out is None:
+        out = torch.empty((B, Lq, H, D), dtype=torch.bfloat16, device=quant.q.device)
+    st = quant.struct()
+    _check(lib().sattn_fwd(ctypes.byref(st), B, H, Lq, Lk, D, float(sm_scale), _view(out, BF16Out),
+                           _stream(stream)), "sattn_fwd")
+    return out
+
+
+def fwd_workspace(nseg, device="cuda"):
+    s = sattn_quant_query(nseg, 0, 0, 1)
+    return torch.empty(s.fwd_workspace_bytes, dtype=torch.uint8, device=device)
+
+
+def sattn_fwd_varlen(quant, cu_seqlens_q, cu_seqlens_k, total_q, sm_scale, out=None, workspace=None, stream=None):
+    """Packed forward; returns (or fills) a BF16 [total_q, H, D] tensor."""
+    nseg = cu_seqlens_q.numel() - 1
+    H = quant.H
+    if out is None:
+        out = torch.empty((total_q, H, D), dtype=torch.bfloat16, device=quant.q.device)
+    if workspace is None:
+        workspace = fwd_workspace(nseg, device=quant.q.device)
+    st = quant.struct()
+    _check(lib().sattn_fwd_varlen(ctypes.byref(st), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), nseg, total_q, H, D,
+                                  float(sm_scale), _view(out, BF16Out), workspace.data_ptr(), workspace.numel(),
+                                  _stream(stream)), "sattn_fwd_varlen")
+    return out
+
+
+def sattn_debug_scores(quant, B, H, Lq, Lk, sm_scale, seg, head, out=None, stream=None):
+    """INT32 accumulators and FP32 scores of one (segment, head): ([Lq, Lk] int32, [Lq, Lk] float32, O)."""
+    dev = quant.q.device
+    acc = torch.empty((Lq, Lk), dtype=torch.int32, device=dev)
+    s = torch.empty((Lq, Lk), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((B, Lq, H, D), dtype=torch.bfloat16, device=dev)
+    st = quant.struct()
+    _check(lib().sattn_debug_scores(ctypes.byref(st), B, H, Lq, Lk, D, float(sm_scale), seg, head, acc.data_ptr(),
+                                    s.data_ptr(), _view(out, BF16Out), _stream(stream)), "sattn_debug_scores")
+    return acc, s, out
+
+
+# ---------------------------------------------------------------- layout inspection
+def untile_qk(tiles):
+    """[nblk, 8192] INT8 operand tiles (one head) → [nblk*64, 128] token-major codes."""
+    t = np.asarray(tiles).reshape(-1, 2, 4, 2, 32, 16)  # [blk, t, u, g, i, s]
+    return t.transpose(0, 1, 4, 3, 2, 5).reshape(-1, 128)  # token = 32t + i, channel = 64g + 16u + s
+
+
+def untile_v(tiles):
+    """[nblk, 8192] E4M3 V tiles (one head) → [nblk*64, 128] token-major codes."""
+    t = np.asarray(tiles).reshape(-1, 4, 2, 2, 32, 4, 4)  # [blk, w, f, g, i, q, r]
+    # key = 32f + 8q + 4g + r, channel = 32w + i
+    return t.transpose(0, 2, 5, 3, 6, 1, 4).reshape(-1, 128)
+
+
+def segment_blocks(cu, dense_L=None):
+    """First quantized block of every segment (dense: s*ceil(L/64); packed: cu[s]//64 + s)."""
+    if dense_L is not None:
+        nb = -(-dense_L // 64)
+        return [s * nb for s in range(len(cu) - 1)]
+    return [int(cu[s]) // 64 + s for s in range(len(cu) - 1)]

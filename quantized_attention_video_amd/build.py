@@ -1,0 +1,43 @@
+"""Build libsattn.so (the C-ABI library of include/sattn.h) in-tree with hipcc for gfx950.
+
+Usage: python -m quantized_attention_video_amd.build
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libsattn.so")
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.hip", "quant.hip", "attn.hip")]
+FLAGS = [
+    "-O3",
+    "--offload-arch=gfx950",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-fvisibility=hidden",
+    "-ffp-contract=off",  # every FP32 rounding step is written out; FMAs are explicit
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",  # no packed FP32 VALU ops
+    "-Wall",
+]
+
+
+def build(verbose=False):
+    """Compile every HIP source into LIB (atomically replaced); raises on failure."""
+    tmp = LIB + ".tmp"
+    cmd = ["hipcc", *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"), *SOURCES,
+           "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines()
+            if "packed-fp32-ops" not in ln and "--hip-link" not in ln and ln.strip()]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs), file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

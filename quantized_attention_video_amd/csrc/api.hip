@@ -1,0 +1,216 @@
+// C ABI of the library (declared in include/sattn.h): argument validation, buffer
+// geometry and kernel launches.  Validation happens before any HIP call, so a call that
+// fails it has enqueued nothing; this part runs (and is tested) without a GPU.
+#include <math.h>
+#include <string.h>
+
+#include "launch.h"
+#include "sattn.h"
+
+using namespace sattn;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool view_ok(const void* ptr, int64_t sb, int64_t st, int64_t sh, bool dense) {
+  if (ptr == nullptr || !aligned16(ptr)) return false;
+  if (st < 0 || sh < 0 || (st % 8) || (sh % 8)) return false;
+  if (dense && (sb < 0 || (sb % 8))) return false;
+  return true;
+}
+
+struct QuantWs {
+  size_t sums, vmax, vinv, total;
+};
+
+QuantWs quant_ws(int nseg, int H) {
+  const size_t n = (size_t)nseg * H * stats_chunks(nseg, H) * kD;
+  QuantWs w;
+  w.sums = align_up(n * sizeof(double));
+  w.vmax = align_up(n * sizeof(float));
+  w.vinv = align_up((size_t)nseg * H * kD * sizeof(float));
+  w.total = w.sums + w.vmax + w.vinv;
+  return w;
+}
+
+size_t fwd_ws(int nseg) { return align_up((size_t)nseg * 4) + align_up(((size_t)nseg + 1) * 4); }
+
+bool quant_bufs_ok(const sattn_qkv_quant* b) {
+  return b && b->q && b->q_scale && b->k && b->k_scale && b->k_mean && b->v && b->v_scale && aligned16(b->q) &&
+         aligned16(b->k) && aligned16(b->v) && b->qblk_cap >= 0 && b->kblk_cap >= 0;
+}
+
+int64_t ceil64(int64_t n) { return (n + 63) / 64; }
+
+// Largest token count whose blocks fit a capacity (cap = floor(T/64) + nseg).
+int64_t clip_for_cap(int64_t cap, int nseg) { return cap >= nseg ? (cap - nseg) * 64 + 63 : 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* sattn_status_string(sattn_status s) {
+  switch (s) {
+    case SATTN_OK: return "ok";
+    case SATTN_EINVAL: return "invalid argument";
+    case SATTN_EUNSUPPORTED: return "unsupported configuration";
+    case SATTN_ENOSPACE: return "buffer or workspace too small";
+    case SATTN_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+sattn_status sattn_quant_query(int nseg, int64_t total_q, int64_t total_k, int H, int D, sattn_sizes* out) {
+  if (out == nullptr || nseg < 1 || H < 1 || total_q < 0 || total_k < 0) return SATTN_EINVAL;
+  if (D != kD) return SATTN_EUNSUPPORTED;
+  memset(out, 0, sizeof(*out));
+  out->qblk_cap = total_q / 64 + nseg;
+  out->kblk_cap = total_k / 64 + nseg;
+  out->q_bytes = (size_t)H * out->qblk_cap * kTileBytes;
+  out->q_scale_bytes = (size_t)H * out->qblk_cap * sizeof(float);
+  out->k_bytes = (size_t)H * out->kblk_cap * kTileBytes;
+  out->k_scale_bytes = (size_t)H * out->kblk_cap * sizeof(float);
+  out->k_mean_bytes = (size_t)nseg * H * kD * sizeof(float);
+  out->v_bytes = out->k_bytes;
+  out->v_scale_bytes = out->k_mean_bytes;
+  out->quant_workspace_bytes = quant_ws(nseg, H).total;
+  out->fwd_workspace_bytes = fwd_ws(nseg);
+  return SATTN_OK;
+}
+
+sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in v, int nseg, int H, int D, int64_t Lq,
+                                int64_t Lk, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                const sattn_qkv_quant* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (nseg < 1 || H < 1 || Lq < 0 || Lk < 0) return SATTN_EINVAL;
+  if (D != kD || nseg > 65535 || H > 65535) return SATTN_EUNSUPPORTED;  // grid y/z extents
+  const bool varlen = cu_seqlens_q != nullptr;
+  if ((cu_seqlens_k != nullptr) != varlen) return SATTN_EINVAL;
+  if (!view_ok(q.ptr, q.stride_b, q.stride_t, q.stride_h, !varlen) ||
+      !view_ok(k.ptr, k.stride_b, k.stride_t, k.stride_h, !varlen) ||
+      !view_ok(v.ptr, v.stride_b, v.stride_t, v.stride_h, !varlen))
+    return SATTN_EINVAL;
+  if (!quant_bufs_ok(out) || workspace == nullptr || !aligned16(workspace)) return SATTN_EINVAL;
+  const int64_t total_q = varlen ? Lq : (int64_t)nseg * Lq;
+  const int64_t total_k = varlen ? Lk : (int64_t)nseg * Lk;
+  if (out->qblk_cap < total_q / 64 + nseg || out->kblk_cap < total_k / 64 + nseg) return SATTN_ENOSPACE;
+  const QuantWs ws = quant_ws(nseg, H);
+  if (workspace_bytes < ws.total) return SATTN_ENOSPACE;
+
+  QuantLaunch a;
+  a.q = static_cast<const uint16_t*>(q.ptr);
+  a.k = static_cast<const uint16_t*>(k.ptr);
+  a.v = static_cast<const uint16_t*>(v.ptr);
+  a.gq = SegGeom{cu_seqlens_q, nseg, Lq, q.stride_b};
+  a.gk = SegGeom{cu_seqlens_k, nseg, Lk, k.stride_b};
+  a.gv = SegGeom{cu_seqlens_k, nseg, Lk, v.stride_b};
+  a.q_st = q.stride_t; a.q_sh = q.stride_h;
+  a.k_st = k.stride_t; a.k_sh = k.stride_h;
+  a.v_st = v.stride_t; a.v_sh = v.stride_h;
+  a.nseg = nseg;
+  a.H = H;
+  a.q_blocks = varlen ? out->qblk_cap : nseg * ceil64(Lq);
+  a.k_blocks = varlen ? out->kblk_cap : nseg * ceil64(Lk);
+  a.q8 = out->q; a.q_scale = out->q_scale;
+  a.k8 = out->k; a.k_scale = out->k_scale; a.k_mean = out->k_mean;
+  a.v8 = out->v; a.v_scale = out->v_scale;
+  a.qblk_cap = out->qblk_cap; a.kblk_cap = out->kblk_cap;
+  a.workspace = workspace;
+  a.ws_sums_bytes = ws.sums;
+  a.ws_vmax_bytes = ws.vmax;
+  if (a.q_blocks > 0x7fffffff || a.k_blocks > 0x7fffffff) return SATTN_EUNSUPPORTED;
+  return launch_quantize(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SATTN_OK : SATTN_EHIP;
+}
+
+static sattn_status fwd_common(const sattn_qkv_quant* qkv, int H, int D, float sm_scale, sattn_bf16_out o,
+                               bool dense) {
+  if (H < 1) return SATTN_EINVAL;
+  if (D != kD) return SATTN_EUNSUPPORTED;
+  if (!quant_bufs_ok(qkv)) return SATTN_EINVAL;
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return SATTN_EINVAL;
+  if (!view_ok(o.ptr, o.stride_b, o.stride_t, o.stride_h, dense)) return SATTN_EINVAL;
+  return SATTN_OK;
+}
+
+static float log2e_scale(float sm_scale) { return (float)((double)sm_scale * 1.4426950408889634); }
+
+static sattn_status fwd_dense(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D, float sm_scale,
+                              sattn_bf16_out o, int dump_seg, int dump_head, int32_t* acc_out, float* s_out,
+                              void* stream) {
+  if (B < 1 || Lq < 0 || Lk < 0) return SATTN_EINVAL;
+  sattn_status st = fwd_common(qkv, H, D, sm_scale, o, true);
+  if (st != SATTN_OK) return st;
+  if (qkv->qblk_cap < (int64_t)B * ceil64(Lq) || qkv->kblk_cap < (int64_t)B * ceil64(Lk)) return SATTN_ENOSPACE;
+  AttnParams p;
+  memset(&p, 0, sizeof(p));
+  p.q8 = qkv->q; p.q_scale = qkv->q_scale;
+  p.k8 = qkv->k; p.k_scale = qkv->k_scale;
+  p.v8 = qkv->v; p.v_scale = qkv->v_scale;
+  p.qblk_cap = qkv->qblk_cap; p.kblk_cap = qkv->kblk_cap;
+  p.H = H; p.nseg = B;
+  p.gq = SegGeom{nullptr, B, Lq, o.stride_b};
+  p.gk = SegGeom{nullptr, B, Lk, 0};
+  p.c32 = log2e_scale(sm_scale);
+  p.o = static_cast<uint16_t*>(o.ptr);
+  p.o_st = o.stride_t; p.o_sh = o.stride_h;
+  p.dump_acc = acc_out; p.dump_s = s_out;
+  p.dump_seg = dump_seg; p.dump_head = dump_head; p.dump_lk = Lk;
+  const int qpw = attn_queries_per_wg();
+  const int64_t ntile = ceil64(Lq) * 64 / qpw + (ceil64(Lq) * 64 % qpw != 0);
+  const int64_t grid = 8 * (int64_t)((H + 7) / 8) * B * ntile;
+  if (grid > 0x7fffffff) return SATTN_EUNSUPPORTED;
+  return launch_attention(p, grid, acc_out != nullptr, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SATTN_OK
+             : SATTN_EHIP;
+}
+
+sattn_status sattn_fwd(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D, float sm_scale,
+                       sattn_bf16_out o, void* stream) {
+  return fwd_dense(qkv, B, H, Lq, Lk, D, sm_scale, o, -1, -1, nullptr, nullptr, stream);
+}
+
+sattn_status sattn_debug_scores(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D, float sm_scale,
+                                int seg, int head, int32_t* acc_out, float* s_out, sattn_bf16_out o, void* stream) {
+  if (acc_out == nullptr || s_out == nullptr || seg < 0 || seg >= B || head < 0 || head >= H) return SATTN_EINVAL;
+  return fwd_dense(qkv, B, H, Lq, Lk, D, sm_scale, o, seg, head, acc_out, s_out, stream);
+}
+
+sattn_status sattn_fwd_varlen(const sattn_qkv_quant* qkv, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int nseg, int64_t total_q, int H, int D, float sm_scale, sattn_bf16_out o,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (nseg < 1 || total_q < 0 || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return SATTN_EINVAL;
+  sattn_status st = fwd_common(qkv, H, D, sm_scale, o, false);
+  if (st != SATTN_OK) return st;
+  if (workspace == nullptr || !aligned16(workspace)) return SATTN_EINVAL;
+  if (workspace_bytes < fwd_ws(nseg)) return SATTN_ENOSPACE;
+  if (qkv->qblk_cap < nseg || qkv->kblk_cap < nseg) return SATTN_ENOSPACE;
+  int32_t* order = static_cast<int32_t*>(workspace);
+  int32_t* tpref = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align_up((size_t)nseg * 4));
+  const int64_t q_clip = total_q < clip_for_cap(qkv->qblk_cap, nseg) ? total_q : clip_for_cap(qkv->qblk_cap, nseg);
+  const int64_t k_clip = clip_for_cap(qkv->kblk_cap, nseg);
+  AttnParams p;
+  memset(&p, 0, sizeof(p));
+  p.q8 = qkv->q; p.q_scale = qkv->q_scale;
+  p.k8 = qkv->k; p.k_scale = qkv->k_scale;
+  p.v8 = qkv->v; p.v_scale = qkv->v_scale;
+  p.qblk_cap = qkv->qblk_cap; p.kblk_cap = qkv->kblk_cap;
+  p.H = H; p.nseg = nseg;
+  p.gq = SegGeom{cu_seqlens_q, nseg, q_clip, 0};
+  p.gk = SegGeom{cu_seqlens_k, nseg, k_clip, 0};
+  p.order = order; p.tpref = tpref;
+  p.c32 = log2e_scale(sm_scale);
+  p.o = static_cast<uint16_t*>(o.ptr);
+  p.o_st = o.stride_t; p.o_sh = o.stride_h;
+  p.dump_seg = -1; p.dump_head = -1;
+  const int64_t tiles_bound = q_clip / attn_queries_per_wg() + nseg + 1;
+  const int64_t grid = 8 * (int64_t)((H + 7) / 8) * tiles_bound;
+  if (grid > 0x7fffffff) return SATTN_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_plan(cu_seqlens_q, cu_seqlens_k, nseg, q_clip, k_clip, order, tpref, s) != hipSuccess) return SATTN_EHIP;
+  return launch_attention(p, grid, false, s) == hipSuccess ? SATTN_OK : SATTN_EHIP;
+}
+
+}  // extern "C"

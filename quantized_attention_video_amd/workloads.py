@@ -121,10 +121,11 @@ def make_inputs(w: Workload, seed: Optional[int] = None, scale_L: Optional[int] 
     q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
     if w.layout == "bhld":  # contiguous [B, H, L, D] storage, viewed as [B, L, H, D]
         q, k, v = (t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for t in (q, k, v))
-    elif w.layout == "fused_qkv":  # slices of one contiguous [B, L, 3, H, D] tensor
+    fused = None
+    if w.layout == "fused_qkv":  # slices of one contiguous [B, L, 3, H, D] tensor
         fused = torch.stack([q, k, v], dim=2).contiguous()
         q, k, v = fused[:, :, 0], fused[:, :, 1], fused[:, :, 2]
-    out = dict(q=q, k=k, v=v, workload=w)
+    out = dict(q=q, k=k, v=v, workload=w, fused=fused)
     if w.varlen:
         out["cu_q"] = w.cu_q()
         out["cu_k"] = w.cu_k()
@@ -132,6 +133,18 @@ def make_inputs(w: Workload, seed: Optional[int] = None, scale_L: Optional[int] 
         Lq, Lk = shapes[0][1], shapes[1][1]
         out["cu_q"] = _prefix([Lq] * w.B)
         out["cu_k"] = _prefix([Lk] * w.B)
+    return out
+
+
+def to_device(inp, device="cuda"):
+    """Copy q, k, v to `device` keeping their strides (the fused QKV storage moves whole)."""
+    out = dict(inp)
+    if inp.get("fused") is not None:
+        f = inp["fused"].to(device)
+        out.update(fused=f, q=f[:, :, 0], k=f[:, :, 1], v=f[:, :, 2])
+    else:
+        for n in ("q", "k", "v"):
+            out[n] = inp[n].to(device)  # dense non-overlapping views keep their strides
     return out
 
 

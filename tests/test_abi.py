@@ -1,0 +1,135 @@
+"""The C-ABI library without a GPU: it loads, exports what include/sattn.h declares, and its
+host-side validation returns the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_attention_video_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sattn.h")
+
+# Never dereferenced: every call below fails validation before any HIP call.
+FAKE = 0x10000
+MISALIGNED = 0x10008
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"SATTN_API\s+[\w\s\*]+?\b(sattn_\w+)\s*\(", text)
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTED)
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    assert B.status_string(B.SATTN_OK) == "ok"
+    assert B.status_string(B.SATTN_ENOSPACE) == "buffer or workspace too small"
+    assert B.status_string(99) == "unknown status"
+
+
+def test_quant_query_sizes():
+    s = B.sattn_quant_query(1, 37810, 37810, 32)
+    assert s.qblk_cap == 37810 // 64 + 1 == 591
+    assert s.q_bytes == 32 * 591 * 8192 and s.q_scale_bytes == 32 * 591 * 4
+    assert s.k_mean_bytes == 32 * 128 * 4 and s.v_bytes == s.k_bytes
+    v = B.sattn_quant_query(4, 47638, 47638, 24)
+    assert v.kblk_cap == 47638 // 64 + 4
+    assert v.fwd_workspace_bytes >= 4 * 4 + 5 * 4
+    with pytest.raises(B.SattnError) as e:
+        B.sattn_quant_query(0, 10, 10, 1)
+    assert e.value.status == B.SATTN_EINVAL
+    with pytest.raises(B.SattnError) as e:
+        B.sattn_quant_query(1, 10, 10, 1, 64)
+    assert e.value.status == B.SATTN_EUNSUPPORTED
+
+
+def test_capacity_bound_covers_every_segment_layout():
+    # blocks of segment s start at cu[s]//64 + s; the last one must end inside the capacity
+    import random
+    rng = random.Random(5)
+    for _ in range(2000):
+        lens = [rng.choice([0, 1, 63, 64, 65, rng.randint(0, 5000)]) for _ in range(rng.randint(1, 12))]
+        cu = [0]
+        for n in lens:
+            cu.append(cu[-1] + n)
+        cap = cu[-1] // 64 + len(lens)
+        ends = [cu[s] // 64 + s + -(-lens[s] // 64) for s in range(len(lens))]
+        starts = [cu[s] // 64 + s for s in range(len(lens))]
+        assert max(ends) <= cap
+        assert all(ends[s] <= starts[s + 1] for s in range(len(lens) - 1))
+
+
+def _quant_struct(cap=100, ptr=FAKE):
+    return B.QKVQuant(ptr, ptr, ptr, ptr, ptr, ptr, ptr, cap, cap)
+
+
+def _in(ptr=FAKE, sb=0, st=128, sh=128):
+    return B.BF16In(ptr, sb, st, sh)
+
+
+def _out(ptr=FAKE, sb=0, st=128, sh=128):
+    return B.BF16Out(ptr, sb, st, sh)
+
+
+def test_quantize_validation():
+    L = B.lib()
+    q = _quant_struct()
+
+    def call(qv=_in(), kv=_in(), vv=_in(), nseg=1, H=1, D=128, Lq=64, Lk=64, cuq=None, cuk=None, out=q, ws=FAKE,
+             wsb=1 << 20):
+        return L.sattn_quantize_qkv(qv, kv, vv, nseg, H, D, Lq, Lk, cuq, cuk, ctypes.byref(out) if out else None,
+                                    ws, wsb, None)
+
+    assert call(D=64) == B.SATTN_EUNSUPPORTED
+    assert call(nseg=0) == B.SATTN_EINVAL
+    assert call(Lq=-1) == B.SATTN_EINVAL
+    assert call(qv=_in(ptr=0)) == B.SATTN_EINVAL
+    assert call(kv=_in(ptr=MISALIGNED)) == B.SATTN_EINVAL
+    assert call(vv=_in(st=100)) == B.SATTN_EINVAL  # token stride not a multiple of 8
+    assert call(cuq=FAKE) == B.SATTN_EINVAL  # only one of the two cu_seqlens
+    assert call(out=None) == B.SATTN_EINVAL
+    assert call(ws=None) == B.SATTN_EINVAL
+    assert call(out=_quant_struct(cap=1)) == B.SATTN_ENOSPACE
+    assert call(wsb=16) == B.SATTN_ENOSPACE
+
+
+def test_fwd_validation():
+    L = B.lib()
+    q = _quant_struct()
+    f = L.sattn_fwd
+    assert f(ctypes.byref(q), 1, 1, 64, 64, 64, 0.1, _out(), None) == B.SATTN_EUNSUPPORTED
+    assert f(ctypes.byref(q), 0, 1, 64, 64, 128, 0.1, _out(), None) == B.SATTN_EINVAL
+    assert f(ctypes.byref(q), 1, 1, 64, 64, 128, 0.0, _out(), None) == B.SATTN_EINVAL
+    assert f(ctypes.byref(q), 1, 1, 64, 64, 128, float("nan"), _out(), None) == B.SATTN_EINVAL
+    assert f(ctypes.byref(q), 1, 1, 64, 64, 128, 0.1, _out(ptr=MISALIGNED), None) == B.SATTN_EINVAL
+    assert f(ctypes.byref(q), 1, 1, 64, 64, 128, 0.1, _out(st=4), None) == B.SATTN_EINVAL
+    assert f(ctypes.byref(_quant_struct(cap=0)), 2, 1, 64, 64, 128, 0.1, _out(), None) == B.SATTN_ENOSPACE
+    assert f(None, 1, 1, 64, 64, 128, 0.1, _out(), None) == B.SATTN_EINVAL
+    v = L.sattn_fwd_varlen
+    assert v(ctypes.byref(q), FAKE, FAKE, 2, 100, 1, 128, 0.1, _out(), FAKE, 4, None) == B.SATTN_ENOSPACE
+    assert v(ctypes.byref(q), None, FAKE, 2, 100, 1, 128, 0.1, _out(), FAKE, 1024, None) == B.SATTN_EINVAL
+    assert v(ctypes.byref(q), FAKE, FAKE, 2, 100, 1, 128, 0.1, _out(), None, 1024, None) == B.SATTN_EINVAL
+    d = L.sattn_debug_scores
+    assert d(ctypes.byref(q), 1, 1, 64, 64, 128, 0.1, 1, 0, FAKE, FAKE, _out(), None) == B.SATTN_EINVAL
+    assert d(ctypes.byref(q), 1, 1, 64, 64, 128, 0.1, 0, 0, None, FAKE, _out(), None) == B.SATTN_EINVAL
+
+
+def test_untile_layouts_are_permutations():
+    import numpy as np
+    idx = np.arange(8192).reshape(1, 8192)
+    a = B.untile_qk(idx)
+    b = B.untile_v(idx)
+    assert sorted(a.ravel().tolist()) == list(range(8192)) == sorted(b.ravel().tolist())
+    # spot-check the documented byte formulas
+    t, u, g, i, s = 1, 2, 1, 5, 7
+    assert a[32 * t + i, 64 * g + 16 * u + s] == ((t * 4 + u) * 64 + g * 32 + i) * 16 + s
+    w, f, g, i, s = 3, 1, 0, 9, 13
+    assert b[32 * f + 8 * (s // 4) + 4 * g + s % 4, 32 * w + i] == ((w * 2 + f) * 64 + g * 32 + i) * 16 + s

@@ -1,0 +1,229 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Bars: quantized bytes and scales bit-exact; INT32 accumulators and FP32 scores bit-exact;
+BF16 output within max|o - r| / max|r| <= 1e-2 and mean|o - r| <= 1e-3 per (segment,
+head) — the tolerance stated for this method — plus exact invariants of the program.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sattn as O
+from quantized_attention_video_amd import binding as B
+from quantized_attention_video_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL = 1e-2
+MAE = 1e-3
+
+
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _sample_rows(L, full_below=2100):
+    """All rows of short sequences; first, middle and last 64-row blocks of long ones."""
+    if L <= full_below:
+        return np.arange(L)
+    mid = (L // 2) // 64 * 64
+    last = (L - 1) // 64 * 64
+    return np.unique(np.concatenate([np.arange(0, 64), np.arange(mid, mid + 64), np.arange(last, L)]))
+
+
+def _tensor_cu(cu):
+    return torch.tensor(cu, dtype=torch.int32, device="cuda")
+
+
+def gpu_run(inp, sm_scale):
+    """Quantize + forward on the GPU for a workload input dict; returns (quant, out)."""
+    w = inp["workload"]
+    dev = W.to_device(inp)
+    if w.varlen:
+        cq, ck = _tensor_cu(inp["cu_q"]), _tensor_cu(inp["cu_k"])
+        quant = B.sattn_quantize_qkv(dev["q"], dev["k"], dev["v"], cq, ck)
+        out = B.sattn_fwd_varlen(quant, cq, ck, dev["q"].shape[0], sm_scale)
+    else:
+        quant = B.sattn_quantize_qkv(dev["q"], dev["k"], dev["v"])
+        Bn, Lq, H = dev["q"].shape[:3]
+        out = B.sattn_fwd(quant, Bn, H, Lq, dev["k"].shape[1], sm_scale)
+    torch.cuda.synchronize()
+    return quant, out
+
+
+@functools.lru_cache(maxsize=8)
+def case(name):
+    """GPU results and oracle quantization of one workload (cached for the session)."""
+    _need_gpu()
+    w = W.get(name)
+    _say(f"[case] {name}: generate + GPU")
+    inp = W.make_inputs(w)
+    quant, out = gpu_run(inp, w.sm_scale)
+    _say(f"[case] {name}: oracle quantize")
+    q64, k64, v64 = (W.packed_float64(inp[n]) for n in "qkv")
+    oq = O.quantize(q64, k64, v64, inp["cu_q"], inp["cu_k"])
+    return dict(w=w, inp=inp, quant=quant, out=out, oq=oq)
+
+
+def _blocks(cu, w):
+    return B.segment_blocks(cu, None if w.varlen else (cu[1] - cu[0]))
+
+
+NAMES = ["fixed_q128_kv192", "dense_h8_l4096", "ragged_b2_h16_l1000", "ragged_b2_h16_l2049", "varlen_h24_4seg",
+         "h3_video_l37810"]
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_quantized_buffers_bit_exact(name):
+    c = case(name)
+    w, quant, oq, inp = c["w"], c["quant"], c["oq"], c["inp"]
+    qt, kt, vt = (getattr(quant, n).cpu().numpy() for n in ("q", "k", "v"))
+    qs, ks = quant.q_scale.cpu().numpy(), quant.k_scale.cpu().numpy()
+    km, vs = quant.k_mean.cpu().numpy(), quant.v_scale.cpu().numpy()
+    bq, bk = _blocks(inp["cu_q"], w), _blocks(inp["cu_k"], w)
+    for si, seg in enumerate(oq):
+        Lq, Lk = seg["q8"].shape[0], seg["k8"].shape[0]
+        nq, nk = -(-Lq // 64), -(-Lk // 64)
+        assert np.array_equal(km[si], seg["k_mean"].astype(np.float32)), f"k_mean seg {si}"
+        assert np.array_equal(vs[si], seg["v_scale"].astype(np.float32)), f"v_scale seg {si}"
+        for h in range(w.H):
+            gq = B.untile_qk(qt[h, bq[si]:bq[si] + nq])
+            gk = B.untile_qk(kt[h, bk[si]:bk[si] + nk])
+            gv = B.untile_v(vt[h, bk[si]:bk[si] + nk])
+            assert np.array_equal(gq[:Lq], seg["q8"][:, h, :].astype(np.int8)), f"q8 seg {si} head {h}"
+            assert np.array_equal(gk[:Lk], seg["k8"][:, h, :].astype(np.int8)), f"k8 seg {si} head {h}"
+            assert np.array_equal(gv[:Lk], seg["v8"][:, h, :]), f"v8 seg {si} head {h}"
+            assert not gq[Lq:].any() and not gk[Lk:].any() and not gv[Lk:].any(), "padding must be zero"
+            assert np.array_equal(qs[h, bq[si]:bq[si] + nq], seg["q_scale"][h].astype(np.float32))
+            assert np.array_equal(ks[h, bk[si]:bk[si] + nk], seg["k_scale"][h].astype(np.float32))
+
+
+@pytest.mark.parametrize("name,seg,head", [("fixed_q128_kv192", 0, 0), ("dense_h8_l4096", 0, 5),
+                                           ("ragged_b2_h16_l1000", 1, 9), ("ragged_b2_h16_l2049", 1, 3)])
+def test_scores_bit_exact(name, seg, head):
+    c = case(name)
+    w = c["w"]
+    Bn, Lq, H = c["inp"]["q"].shape[:3]
+    Lk = c["inp"]["k"].shape[1]
+    acc, s, out = B.sattn_debug_scores(c["quant"], Bn, H, Lq, Lk, w.sm_scale, seg, head)
+    torch.cuda.synchronize()
+    r_acc, r_s = O.scores(c["oq"][seg], head, w.sm_scale)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), r_acc.astype(np.int64))
+    assert np.array_equal(s.cpu().numpy(), r_s.astype(np.float32))
+    # the dump run computes the same forward output as the plain run
+    assert torch.equal(out, c["out"])
+
+
+def _check_output(got, ref, label):
+    for h in range(ref.shape[1]):
+        err = np.abs(got[:, h] - ref[:, h])
+        scale = np.max(np.abs(ref[:, h]))
+        assert np.max(err) <= MAX_REL * scale, f"{label} head {h}: max rel {np.max(err) / scale:.3e}"
+        assert np.mean(err) <= MAE, f"{label} head {h}: mae {np.mean(err):.3e}"
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_output_within_tolerance(name):
+    c = case(name)
+    w, oq, inp = c["w"], c["oq"], c["inp"]
+    out = c["out"].float().cpu()
+    rows = {si: _sample_rows(seg["q8"].shape[0]) for si, seg in enumerate(oq)}
+    _say(f"[oracle] {name}: attention on {sum(len(r) for r in rows.values())} rows per head")
+    ref = O.attention(oq, w.sm_scale, rows=rows)
+    for si, (a, b) in enumerate(O.segments(inp["cu_q"])):
+        if w.varlen:
+            got = out[a:b].numpy()
+        else:
+            got = out[si].numpy()
+        _check_output(got[rows[si]].astype(np.float64), ref[si], f"{name} seg {si}")
+    assert torch.isfinite(c["out"].float()).all()
+
+
+def test_varlen_equals_per_segment_dense():
+    _need_gpu()
+    rng = torch.Generator().manual_seed(7)
+    lens = [70, 1, 0, 129, 300, 64]
+    T, H = sum(lens), 3
+    q, k, v = (torch.randn((T, H, 128), generator=rng).to(torch.bfloat16) for _ in range(3))
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    cq = _tensor_cu(cu)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    quant = B.sattn_quantize_qkv(qd, kd, vd, cq, cq)
+    joint = B.sattn_fwd_varlen(quant, cq, cq, T, 128 ** -0.5)
+    for s, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        if b == a:
+            continue
+        qs, ks, vs = (t[a:b].unsqueeze(0) for t in (qd, kd, vd))
+        part = B.sattn_fwd(B.sattn_quantize_qkv(qs, ks, vs), 1, H, b - a, b - a, 128 ** -0.5)
+        assert torch.equal(joint[a:b], part[0]), f"segment {s}"
+
+
+def test_v_power_of_two_scaling_is_exact():
+    c = case("ragged_b2_h16_l1000")
+    w = c["w"]
+    inp = dict(c["inp"])
+    inp["v"] = inp["v"] * 8.0  # exact in BF16
+    _, out = gpu_run(inp, w.sm_scale)
+    assert torch.equal(out.float(), c["out"].float() * 8.0)
+
+
+def test_repeated_launches_are_bitwise_identical():
+    c = case("dense_h8_l4096")
+    w = c["w"]
+    _, out = gpu_run(c["inp"], w.sm_scale)
+    for _ in range(20):
+        o2 = B.sattn_fwd(c["quant"], 1, 8, 4096, 4096, w.sm_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, out)
+
+
+@pytest.mark.parametrize("Lq,Lk", [(1, 1), (5, 64), (64, 65), (300, 3), (257, 1000)])
+def test_small_shapes_and_untouched_padding(Lq, Lk):
+    _need_gpu()
+    g = torch.Generator().manual_seed(Lq * 1000 + Lk)
+    H, Bn = 2, 2
+    q = torch.randn((Bn, Lq, H, 128), generator=g).to(torch.bfloat16)
+    k = torch.randn((Bn, Lk, H, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((Bn, Lk, H, 128), generator=g).to(torch.bfloat16)
+    quant = B.sattn_quantize_qkv(q.cuda(), k.cuda(), v.cuda())
+    # write into the middle of a larger canary-filled tensor: nothing else may change
+    big = torch.full((Bn, Lq + 3, H + 1, 256), 7.0, dtype=torch.bfloat16, device="cuda")
+    view = big[:, 1:Lq + 1, :H, 64:192]
+    B.sattn_fwd(quant, Bn, H, Lq, Lk, 0.09, out=view)
+    torch.cuda.synchronize()
+    mask = torch.ones_like(big, dtype=torch.bool)
+    mask[:, 1:Lq + 1, :H, 64:192] = False
+    assert torch.all(big[mask] == 7.0)
+    cu_q = [0, Lq, 2 * Lq]
+    cu_k = [0, Lk, 2 * Lk]
+    oq = O.quantize(W.packed_float64(q), W.packed_float64(k), W.packed_float64(v), cu_q, cu_k)
+    ref = O.attention(oq, 0.09)
+    got = view.float().cpu().reshape(-1, H, 128).numpy().astype(np.float64)
+    for s in range(Bn):
+        _check_output(got[s * Lq:(s + 1) * Lq], ref[s * Lq:(s + 1) * Lq], f"Lq={Lq} Lk={Lk} seg {s}")
+
+
+def test_queries_without_keys_give_zeros():
+    _need_gpu()
+    g = torch.Generator().manual_seed(3)
+    cu_q, cu_k = [0, 5, 10, 80], [0, 0, 7, 7]
+    q = torch.randn((80, 2, 128), generator=g).to(torch.bfloat16)
+    k = torch.randn((7, 2, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((7, 2, 128), generator=g).to(torch.bfloat16)
+    cq, ck = _tensor_cu(cu_q), _tensor_cu(cu_k)
+    quant = B.sattn_quantize_qkv(q.cuda(), k.cuda(), v.cuda(), cq, ck)
+    out = B.sattn_fwd_varlen(quant, cq, ck, 80, 0.1).float().cpu().numpy()
+    assert np.all(out[0:5] == 0) and np.all(out[10:80] == 0)
+    oq = O.quantize(W.packed_float64(q), W.packed_float64(k), W.packed_float64(v), cu_q, cu_k)
+    ref = O.attention(oq, 0.1)
+    _check_output(out[5:10].astype(np.float64), ref[5:10], "seg 1")
+    assert np.all(ref[0:5] == 0) and np.all(ref[10:] == 0)
