@@ -1,0 +1,210 @@
+"""Throughput of the quantized attention hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one batch of synthetic input already resident
+in HBM: sattn_quantize_qkv (K statistics, INT8 Q/K tiles, E4M3 V tiles) followed by
+sattn_fwd (the fused attention kernel).  The default workload is the H3-like video layer:
+B=1, H=32, L=37,810 packed tokens, D=128, Q/K/V projection-strided slices of one fused
+[L, 3, H, D] BF16 tensor.  `value` is 4*Lq*Lk*D*H per step over the measured step time
+(TOPS).  The attention kernel's own launches are timed with HIP events on the stream it
+runs on; its algorithmic operation count over that time, against the 5.0 POP/s dense
+INT8/FP8 MFMA peak, is the roofline entry.  The CPU baseline times the FP64 oracle on a
+bounded sample of the same workload and extrapolates linearly.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TOPS = 5000.0  # MI355X dense INT8 (and FP8) MFMA peak, TOP/s
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_h3_l37810_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "quantized_attention_video_amd", "csrc", "attn.hip")
+
+
+def kernel_source_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, or None
+    if there is none for this workload or the kernel source changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("workload") != workload or kv.get("attn_hip_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, inp, heads=4, rows=128):
+    """Time the oracle on `heads` heads (full-length quantization) and `rows` query rows of
+    attention per head, then extrapolate linearly to the whole step."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import sattn as O
+    from quantized_attention_video_amd import workloads as W
+
+    q, k, v = (W.packed_float64(inp[n][:, :, :heads]) for n in "qkv")
+    t0 = time.perf_counter()
+    quant = O.quantize(q, k, v, inp["cu_q"], inp["cu_k"])
+    t1 = time.perf_counter()
+    L = w.Lq
+    sel = np.concatenate([np.arange(0, rows // 2), np.arange(L - rows // 2, L)])
+    O.attention(quant, w.sm_scale, rows={0: sel})
+    t2 = time.perf_counter()
+    scale_h = w.H / heads
+    est = (t1 - t0) * scale_h + (t2 - t1) * scale_h * (L / rows)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": w.ops() / est / 1e12,
+        "unit": "TOPS",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"FP64 oracle: quantization of {heads}/{w.H} heads over all {L} tokens "
+                   f"({t1 - t0:.1f} s) + attention for {rows} query rows of those heads against all keys "
+                   f"({t2 - t1:.1f} s); extrapolated linearly to the full step = {est:.0f} s"),
+        "cpu": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="h3_video_l37810")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="only run N plain 1 GiB device copies (counter calibration) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calib:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.copy_calib):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each": 1 << 30, "copies": args.copy_calib}))
+        return
+
+    from quantized_attention_video_amd import binding as B
+    from quantized_attention_video_amd import workloads as W
+
+    w = W.get(args.workload)
+    if w.varlen:
+        raise SystemExit("bench.py times dense workloads; the packed one is covered by the GPU tests")
+    inp = W.make_inputs(w)
+    dev = W.to_device(inp)
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    Bn, Lq, H = q.shape[:3]
+    Lk = k.shape[1]
+    quant = B.alloc_quantized(Bn, Bn * Lq, Bn * Lk, H)
+    out = torch.empty((Bn, Lq, H, 128), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        B.sattn_quantize_qkv(q, k, v, out=quant, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        B.sattn_fwd(quant, Bn, H, Lq, Lk, w.sm_scale, out=out, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    quant_ms = [e[0].elapsed_time(e[1]) for e in events]
+    fwd_ms = [e[1].elapsed_time(e[2]) for e in events]
+
+    ops = w.ops()
+    ms_per_step = wall * 1e3 / args.steps
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    quant_avg = sum(quant_ms) / len(quant_ms)
+    achieved = ops / (fwd_avg * 1e-3) / 1e12
+    traffic = measured_traffic(w.name)
+    # algorithmic HBM bytes of the quantization pass: Q read once (2D) and written as INT8
+    # (D); K and V read twice each (statistics, then quantization: 8D) and written once (2D)
+    quant_bytes = H * Bn * (3 * 128 * Lq + 10 * 128 * Lk)
+    result = {
+        "metric": "attention TOPS (4*Lq*Lkv*D*H/s) at L=37,810 D=128; % of MFMA peak",
+        "value": ops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 (QK) + fp8 e4m3 (PV), fp32 softmax",
+        "data": "synthetic (seeded N(0,1) BF16, per-channel K bias N(0,2))",
+        "config": {"workload": w.name, "B": Bn, "H": H, "Lq": Lq, "Lk": Lk, "D": 128,
+                   "layout": w.layout, "step": "sattn_quantize_qkv + sattn_fwd"},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_kernel",
+            "achieved": achieved,
+            "peak": PEAK_TOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_TOPS,
+            "traffic": traffic,
+            "ops_per_launch": ops,
+            "avg_launch_ms": fwd_avg,
+        },
+        "breakdown": {
+            "fwd_ms_avg": fwd_avg,
+            "fwd_ms_min": min(fwd_ms),
+            "quant_ms_avg": quant_avg,
+            "fwd_tops": achieved,
+            "quant_gbs": quant_bytes / (quant_avg * 1e-3) / 1e9,
+            "quant_hbm_frac": quant_bytes / (quant_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

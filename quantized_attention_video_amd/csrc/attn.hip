@@ -24,8 +24,10 @@
 //  * The lane's 32 probabilities are packed with v_cvt_pk_fp8_f32 directly into the B
 //    operand of v_mfma_f32_32x32x64_f8f6f4 (O^T += V^T P^T).  The V tile is stored by the
 //    quantizer with its keys permuted to match, so no probability goes through LDS.
-//  * K and V tiles (8 KiB each per epoch) are streamed into double-buffered LDS with
-//    global_load_lds_dwordx4 (no VGPR staging); one barrier per epoch.
+//  * K and V tiles (8 KiB each per epoch) stream into four LDS stages with
+//    global_load_lds_dwordx4 (no VGPR staging), two epochs ahead; one barrier per epoch.
+//    The P.V MFMAs of epoch e-1 are issued between the exponentials of epoch e (no
+//    dependence between them), so matrix cores and vector ALUs work at the same time.
 //  * The O rescale by alpha is skipped when no row of the wave changed its max (alpha is
 //    then exactly 1, so skipping is bit-identical).
 //  * Work items (segment, head, 256-query tile) are ordered so that consecutive
@@ -56,9 +58,194 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __int_as_float((int)r[0]) + __int_as_float((int)r[1]);
 }
 
+// S^T tile pair of one epoch: acc[t] = K(keys 32t..32t+31) . Q^T over 128 channels.
+__device__ __forceinline__ void qk_epoch(v16i (&acc)[2], const uint8_t* Kl, const v4i (&qop)[4], int lane) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[t][i] = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const v4i a = *reinterpret_cast<const v4i*>(Kl + ((t * 4 + u) * 64 + lane) * 16);
+      acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qop[u], acc[t], 0, 0, 0);
+    }
+  }
+}
+
+// O^T += V^T P^T for one 32-channel tile w.
+__device__ __forceinline__ void pv_tile(v16f& o, const uint8_t* Vl, const v8i& pb, int lane, int w) {
+  const v4i lo = *reinterpret_cast<const v4i*>(Vl + ((w * 2 + 0) * 64 + lane) * 16);
+  const v4i hi = *reinterpret_cast<const v4i*>(Vl + ((w * 2 + 1) * 64 + lane) * 16);
+  const v8i a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  o = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o, 0, 0, 0, 0, 0, 0);
+}
+
+// K/V tiles of four consecutive epochs live in four separate LDS arrays, so that the
+// compiler can tell an LDS-DMA write into one stage from reads of another (one shared
+// array indexed at run time makes it wait for every DMA before any LDS read).
+__shared__ __attribute__((aligned(16))) uint8_t g_stage0[2 * kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_stage1[2 * kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_stage2[2 * kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_stage3[2 * kTileBytes];
+constexpr int kStages = 4;
+constexpr int kLoadsPerThread = 1024 / (kWaves * 64);
+
+template <int ST>
+__device__ __forceinline__ uint8_t* stage() {
+  static_assert(ST >= 0 && ST < kStages, "stage");
+  if constexpr (ST == 0) return g_stage0;
+  if constexpr (ST == 1) return g_stage1;
+  if constexpr (ST == 2) return g_stage2;
+  return g_stage3;
+}
+
+// Per-wave state of the epoch pipeline.
+struct Pipe {
+  v16f oacc[4];  // O^T, 32 channels x 32 queries per tile
+  v4i qop[4];    // Q operand (this wave's 32 queries)
+  v8i pb_prev;   // E4M3 probabilities of the previous epoch (PV deferred by one step)
+  float alpha_prev;  // its rescale factor, applied to O just before its PV is accumulated
+  float m, dpart, sig_q;
+  const float* ksc;
+  const uint8_t *kg, *vg;
+  int lane, wave, g, nkb;
+  bool active;
+};
+
+// Checkpoint dump of the production score accumulators (sattn_debug_scores).
+struct Dump {
+  int32_t* acc;
+  float* s;
+  int64_t lk, row, len_q;
+  bool on;
+};
+
+// Each epoch moves 1024 16-byte chunks (K tile, then V tile) into stage ST; wave w, step
+// j covers chunks j*512 + w*64 + lane, which lie in one tile (wave-uniform LDS base).
+template <int ST>
+__device__ __forceinline__ void issue_tile(const Pipe& c, int e) {
+#pragma unroll
+  for (int j = 0; j < kLoadsPerThread; ++j) {
+    const int c0 = j * kWaves * 64 + c.wave * 64;
+    const int which = c0 >> 9, cw = c0 & 511;
+    const uint8_t* src = (which ? c.vg : c.kg) + (int64_t)e * kTileBytes + (int64_t)(cw + c.lane) * 16;
+    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(stage<ST>() + which * kTileBytes + cw * 16),
+                                     16, 0, 0);
+  }
+}
+
+// Online softmax of one epoch for this lane's query (32 of the 64 keys; the other 32 are
+// in lane ^ 32), with the deferred PV MFMAs of the previous epoch interleaved (they do
+// not depend on it).  Updates m and the lane's partial denominator (in units of 448*P),
+// packs the E4M3 probabilities into pb and returns alpha.  TAIL masks keys >= kvalid.
+template <bool TAIL>
+__device__ __forceinline__ float softmax_pv(Pipe& c, const v16i (&acc)[2], float sig, int kvalid, v8i& pb,
+                                            const uint8_t* Vprev) {
+  const int g = c.g;
+  int mx4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {  // four independent max chains of 8 (t = q/2, rows 8(q%2)..)
+    int v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = q >> 1, r = 8 * (q & 1) + j;
+      const int key = 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+      v[j] = (TAIL && key >= kvalid) ? INT_MIN : acc[t][r];
+    }
+    mx4[q] = max(max(max(v[0], v[1]), max(v[2], v[3])), max(max(v[4], v[5]), max(v[6], v[7])));
+  }
+  int mx = max(max(mx4[0], mx4[1]), max(mx4[2], mx4[3]));
+  mx = xhalf_max(mx);
+  const float smax = (float)mx * sig;  // = max_j fl32(acc_j * sig)
+  const float m_new = fmaxf(c.m, smax);
+  const float alpha = __builtin_amdgcn_exp2f(c.m - m_new);  // 0 on the first epoch
+  const float mm = m_new - kLog2_448;
+  float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {  // chunk w: 8 probabilities, next to PV tile w of epoch e-1
+    pv_tile(c.oacc[w], Vprev, c.pb_prev, c.lane, w);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int t = w >> 1, q4 = 2 * (w & 1) + h2;
+      float pv[4];
+#pragma unroll
+      for (int r3 = 0; r3 < 4; ++r3) {
+        float arg = __builtin_fmaf((float)acc[t][4 * q4 + r3], sig, -mm);
+        if (TAIL && 32 * t + 8 * q4 + 4 * g + r3 >= kvalid) arg = -INFINITY;
+        pv[r3] = __builtin_amdgcn_exp2f(arg);  // 448 * P
+        ps[r3] += pv[r3];
+      }
+      int w01 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+      w01 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w01, true);
+      pb[4 * t + q4] = w01;
+    }
+  }
+  c.dpart = c.dpart * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+  c.m = m_new;
+  return alpha;
+}
+
+// O *= alpha of the epoch whose PV is about to be accumulated (skipped when no row of the
+// wave changed its max: alpha is then exactly 1).
+__device__ __forceinline__ void rescale(Pipe& c) {
+  const float a = c.alpha_prev;
+  if (__any(a != 1.0f)) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c.oacc[w][i] *= a;
+  }
+}
+
+// Pipeline step for epoch e held in stage ST: wait for tile e, start tile e+2, then
+// (active waves) QK(e), the O rescale by alpha(e-1) while those MFMAs run, and the softmax
+// of e interleaved with PV(e-1).  LAST marks the final epoch (no tile e+1 in flight; TAIL
+// masks its keys), which also accumulates its own PV.
+template <int ST, bool LAST, bool TAIL, bool DUMP>
+__device__ __forceinline__ void pipe_step(Pipe& c, int e, int kvalid, const Dump& dump) {
+  constexpr int ST_PREV = (ST + kStages - 1) % kStages, ST_NEXT2 = (ST + 2) % kStages;
+  if constexpr (LAST) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerThread) : "memory");  // tile e+1 may fly
+  __syncthreads();  // tile e visible to every wave; every wave is done with step e-1
+  if (e + 2 < c.nkb) issue_tile<ST_NEXT2>(c, e + 2);
+  if (!c.active) return;
+  v16i acc[2];
+  qk_epoch(acc, stage<ST>(), c.qop, c.lane);
+  rescale(c);  // O = RO(e-2) * alpha(e-1), so PV(e-1) below completes RO(e-1)
+  const float sig = c.sig_q * c.ksc[e];  // fl32(fl32(q_scale * c) * k_scale)
+  if constexpr (DUMP) {
+    if (dump.on && dump.row < dump.len_q) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * t + 8 * (r >> 2) + 4 * c.g + (r & 3);
+          if (key < kvalid) {
+            const int64_t o = dump.row * dump.lk + (int64_t)e * kBlk + key;
+            dump.acc[o] = acc[t][r];
+            dump.s[o] = (float)acc[t][r] * sig;
+          }
+        }
+    }
+  }
+  v8i pb;
+  c.alpha_prev = softmax_pv<TAIL>(c, acc, sig, kvalid, pb, stage<ST_PREV>() + kTileBytes);
+  c.pb_prev = pb;
+  if constexpr (LAST) {
+    rescale(c);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) pv_tile(c.oacc[w], stage<ST>() + kTileBytes, pb, c.lane, w);
+  }
+}
+
+template <int ST, bool DUMP>
+__device__ __forceinline__ void last_step(Pipe& c, int e, int kvalid, const Dump& dump) {
+  if (kvalid == kBlk) pipe_step<ST, true, false, DUMP>(c, e, kBlk, dump);
+  else pipe_step<ST, true, true, DUMP>(c, e, kvalid, dump);
+}
+
 template <bool DUMP>
 __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTileBytes];  // [stage][K, V]
   __shared__ float s_vscale[kD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -93,164 +280,95 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
   const int h = xcd + 8 * (int)hl;
   const SegInfo qi = seg_info(p.gq, s, p.o_st);
   const SegInfo ki = seg_info(p.gk, s, 0);
-  const int64_t nkb = ceil_blocks(ki.len);
+  const int nkb = (int)ceil_blocks(ki.len);
+  const int last_valid = (int)(ki.len - (int64_t)(nkb - 1) * kBlk);  // keys in the last epoch
   const int64_t qb = qt * kQBlocksPerWG + (wave >> 1);  // this wave's 64-query block
   const int hq = wave & 1;                              // and which 32 of its queries
-  const bool active = qb < ceil_blocks(qi.len);
-  const int g = lane >> 5, jq = lane & 31;
 
   if (tid < kD) s_vscale[tid] = p.v_scale[((int64_t)s * p.H + h) * kD + tid];
 
-  // ---------------------------------------------------------------- Q operand (registers)
-  v4i qop[4];
-  float sig_q = 0.f;
-  if (active) {
-    const int8_t* qt_ptr = p.q8 + ((int64_t)h * p.qblk_cap + qi.blk0 + qb) * kTileBytes;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) qop[u] = *reinterpret_cast<const v4i*>(qt_ptr + ((hq * 4 + u) * 64 + lane) * 16);
-    sig_q = p.q_scale[(int64_t)h * p.qblk_cap + qi.blk0 + qb] * p.c32;  // fl32(q_scale * c)
-  } else {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) qop[u] = v4i{0, 0, 0, 0};
-  }
-
-  const int64_t ktile0 = (int64_t)h * p.kblk_cap + ki.blk0;
-  const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.k8) + ktile0 * kTileBytes;
-  const uint8_t* vg = p.v8 + ktile0 * kTileBytes;
-  const float* ksc = p.k_scale + ktile0;
-
-  // Each epoch moves 1024 16-byte chunks (K tile, then V tile); wave w, step j covers
-  // chunks j*512 + w*64 + lane, which lie in one tile, so the LDS base is wave-uniform.
-  auto issue = [&](int64_t e, int stage) {
-#pragma unroll
-    for (int j = 0; j < 1024 / (kWaves * 64); ++j) {
-      const int c0 = j * kWaves * 64 + wave * 64;
-      const int which = c0 >> 9, cw = c0 & 511;
-      const uint8_t* src = (which ? vg : kg) + e * kTileBytes + (int64_t)(cw + lane) * 16;
-      __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)&lds[stage][which][cw * 16], 16, 0, 0);
-    }
-  };
-
-  float m = -INFINITY, dpart = 0.f;
-  v16f oacc[4];
+  Pipe c;
+  c.lane = lane;
+  c.wave = wave;
+  c.g = lane >> 5;
+  c.nkb = nkb;
+  c.active = qb < ceil_blocks(qi.len);
+  c.m = -INFINITY;
+  c.dpart = 0.f;
+  c.sig_q = 0.f;
+  c.alpha_prev = 1.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[w][i] = 0.f;
+    for (int i = 0; i < 16; ++i) c.oacc[w][i] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c.pb_prev[i] = 0;
+  if (c.active) {
+    const int8_t* qt_ptr = p.q8 + ((int64_t)h * p.qblk_cap + qi.blk0 + qb) * kTileBytes;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) c.qop[u] = *reinterpret_cast<const v4i*>(qt_ptr + ((hq * 4 + u) * 64 + lane) * 16);
+    c.sig_q = p.q_scale[(int64_t)h * p.qblk_cap + qi.blk0 + qb] * p.c32;  // fl32(q_scale * c)
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) c.qop[u] = v4i{0, 0, 0, 0};
+  }
+  const int64_t ktile0 = (int64_t)h * p.kblk_cap + ki.blk0;
+  c.kg = reinterpret_cast<const uint8_t*>(p.k8) + ktile0 * kTileBytes;
+  c.vg = p.v8 + ktile0 * kTileBytes;
+  c.ksc = p.k_scale + ktile0;
 
-  if (nkb > 0) issue(0, 0);
-  __syncthreads();  // s_vscale visible even when there are no epochs
-  for (int64_t e = 0; e < nkb; ++e) {
-    const int st = (int)(e & 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // epoch e landed for every wave; every wave is done with epoch e-1
-    if (e + 1 < nkb) issue(e + 1, st ^ 1);
-    if (!active) continue;
+  Dump dump;
+  dump.acc = p.dump_acc;
+  dump.s = p.dump_s;
+  dump.lk = p.dump_lk;
+  dump.row = qb * kBlk + hq * 32 + (lane & 31);
+  dump.len_q = qi.len;
+  dump.on = DUMP && s == p.dump_seg && h == p.dump_head;
 
-    // ---------------- S^T = K Q^T (exact INT32)
-    const uint8_t* Kl = lds[st][0];
-    const uint8_t* Vl = lds[st][1];
-    v16i acc[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[t][i] = 0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const v4i a = *reinterpret_cast<const v4i*>(Kl + ((t * 4 + u) * 64 + lane) * 16);
-        acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qop[u], acc[t], 0, 0, 0);
-      }
+  // ---------------------------------------------------------------- epoch pipeline
+  // Epoch e lives in stage e % 4; step e reads its K tile and the V tile of epoch e-1,
+  // while tile e+2 streams in.  The V half of stage 3 starts as zeros: step 0's deferred
+  // PV multiplies it by all-zero probabilities.
+  reinterpret_cast<v4i*>(stage<3>() + kTileBytes)[tid] = v4i{0, 0, 0, 0};
+  if (nkb > 0) issue_tile<0>(c, 0);
+  if (nkb > 1) issue_tile<1>(c, 1);
+  const int nfull = nkb - 1;  // epochs before the last one
+  int e = 0;
+  for (; e + 4 <= nfull; e += 4) {
+    pipe_step<0, false, false, DUMP>(c, e, kBlk, dump);
+    pipe_step<1, false, false, DUMP>(c, e + 1, kBlk, dump);
+    pipe_step<2, false, false, DUMP>(c, e + 2, kBlk, dump);
+    pipe_step<3, false, false, DUMP>(c, e + 3, kBlk, dump);
+  }
+  if (e < nfull) pipe_step<0, false, false, DUMP>(c, e, kBlk, dump);
+  if (e + 1 < nfull) pipe_step<1, false, false, DUMP>(c, e + 1, kBlk, dump);
+  if (e + 2 < nfull) pipe_step<2, false, false, DUMP>(c, e + 2, kBlk, dump);
+  if (nkb > 0) {
+    switch (nfull & 3) {
+      case 0: last_step<0, DUMP>(c, nfull, last_valid, dump); break;
+      case 1: last_step<1, DUMP>(c, nfull, last_valid, dump); break;
+      case 2: last_step<2, DUMP>(c, nfull, last_valid, dump); break;
+      default: last_step<3, DUMP>(c, nfull, last_valid, dump); break;
     }
-    const float sig = sig_q * ksc[e];  // fl32(fl32(q_scale * c) * k_scale)
-    const int64_t kvalid = ki.len - e * kBlk;
-    const bool tail = kvalid < kBlk;
-
-    if constexpr (DUMP) {
-      if (s == p.dump_seg && h == p.dump_head) {
-        const int64_t row = qb * kBlk + hq * 32 + jq;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (row < qi.len && key < kvalid) {
-              const int a = acc[t][r];
-              p.dump_acc[row * p.dump_lk + e * kBlk + key] = a;
-              p.dump_s[row * p.dump_lk + e * kBlk + key] = (float)a * sig;
-            }
-          }
-      }
-    }
-
-    // ---------------- online softmax (base 2), row max on the integer accumulators
-    int mx = INT_MIN;  // masked keys never win
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-        const int a = (tail && key >= kvalid) ? INT_MIN : acc[t][r];
-        mx = max(mx, a);
-      }
-    mx = xhalf_max(mx);
-    const float smax = (float)mx * sig;  // = max_j fl32(acc_j * sig)
-    const float m_new = fmaxf(m, smax);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first epoch
-    const float mm = m_new - kLog2_448;
-    float psum = 0.f;
-    v8i pb;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float pv[4];
-#pragma unroll
-        for (int r3 = 0; r3 < 4; ++r3) {
-          const int r = 4 * q4 + r3;
-          const int key = 32 * t + 8 * q4 + 4 * g + r3;
-          float arg = __builtin_fmaf((float)acc[t][r], sig, -mm);
-          if (tail && key >= kvalid) arg = -INFINITY;
-          pv[r3] = __builtin_amdgcn_exp2f(arg);  // 448 * P
-          psum += pv[r3];
-        }
-        int w01 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
-        w01 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w01, true);
-        pb[4 * t + q4] = w01;
-      }
-    dpart = dpart * alpha + psum;
-    m = m_new;
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[w][i] *= alpha;
-    }
-
-    // ---------------- O^T += V^T P^T (FP8 x FP8 -> FP32)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const v4i lo = *reinterpret_cast<const v4i*>(Vl + ((w * 2 + 0) * 64 + lane) * 16);
-      const v4i hi = *reinterpret_cast<const v4i*>(Vl + ((w * 2 + 1) * 64 + lane) * 16);
-      const v8i a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      oacc[w] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, oacc[w], 0, 0, 0, 0, 0, 0);
-    }
+  } else {
+    __syncthreads();  // s_vscale visible
   }
 
   // ---------------------------------------------------------------- epilogue
-  if (!active) return;
-  const float dtot = xhalf_sum(dpart);  // = 448 * d
+  if (!c.active) return;
+  const float dtot = xhalf_sum(c.dpart);  // = 448 * d
   const float inv = dtot > 0.f ? 1.0f / dtot : 0.f;
-  const int64_t row = qb * kBlk + hq * 32 + jq;
+  const int64_t row = qb * kBlk + hq * 32 + (lane & 31);
   if (row >= qi.len) return;
   uint16_t* orow = p.o + qi.elem_base + row * p.o_st + (int64_t)h * p.o_sh;
 #pragma unroll
   for (int w = 0; w < 4; ++w)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const int c0 = 32 * w + 8 * q4 + 4 * g;
+      const int c0 = 32 * w + 8 * q4 + 4 * c.g;
       uint32_t b[4];
 #pragma unroll
-      for (int r3 = 0; r3 < 4; ++r3) b[r3] = f32_to_bf16_bits((oacc[w][4 * q4 + r3] * inv) * s_vscale[c0 + r3]);
+      for (int r3 = 0; r3 < 4; ++r3) b[r3] = f32_to_bf16_bits((c.oacc[w][4 * q4 + r3] * inv) * s_vscale[c0 + r3]);
       *reinterpret_cast<uint2*>(orow + c0) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
     }
 }
