@@ -9,9 +9,10 @@
 // softmax occupies the vector pipes).  The pages' GB10 kernel is warp-specialised with
 // mbarriers; this one is designed for CDNA4 instead:
 //
-//  * One workgroup = 8 waves = 256 queries of one (segment, head); each wave owns 32
-//    queries, so two waves share a SIMD and the hardware overlaps one wave's softmax
-//    (VALU) with the other's MFMAs.  Per wave the working set stays under 256 VGPRs.
+//  * One workgroup = 4 waves = 128 queries of one (segment, head); each wave owns 32
+//    queries and stays under 256 VGPRs, so two workgroups share a CU and every SIMD runs
+//    two waves of different workgroups.  Their barriers are independent, so one wave's
+//    softmax (VALU) overlaps the other's MFMAs instead of both stalling in step.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_i32_32x32x32_i8: each lane
 //    owns one query column and 32 of the epoch's 64 keys, so the row max and row sum are
 //    in-lane plus one v_permlane32_swap between the two half-waves.
@@ -25,9 +26,11 @@
 //    operand of v_mfma_f32_32x32x64_f8f6f4 (O^T += V^T P^T).  The V tile is stored by the
 //    quantizer with its keys permuted to match, so no probability goes through LDS.
 //  * K and V tiles (8 KiB each per epoch) stream into four LDS stages with
-//    global_load_lds_dwordx4 (no VGPR staging), two epochs ahead; one barrier per epoch.
-//    The P.V MFMAs of epoch e-1 are issued between the exponentials of epoch e (no
-//    dependence between them), so matrix cores and vector ALUs work at the same time.
+//    global_load_lds_dwordx4 (no VGPR staging); one barrier per epoch.  Between the
+//    exponentials of epoch e the wave issues the P.V MFMAs of epoch e-1 and, as each
+//    score tile of epoch e is consumed, the QK MFMAs of epoch e+1 into the same
+//    registers: no MFMA result is waited for inside a step, and matrix cores and vector
+//    ALUs work at the same time.
 //  * The O rescale by alpha is skipped when no row of the wave changed its max (alpha is
 //    then exactly 1, so skipping is bit-identical).
 //  * Work items (segment, head, 256-query tile) are ordered so that consecutive
@@ -42,7 +45,7 @@
 
 namespace sattn {
 
-constexpr int kWaves = 8;                  // waves per workgroup
+constexpr int kWaves = 4;                  // waves per workgroup (two workgroups per CU)
 constexpr int kQPerWG = kWaves * 32;       // queries per workgroup
 constexpr int kQBlocksPerWG = kWaves / 2;  // 64-query blocks per workgroup
 constexpr float kLog2_448 = 8.8073549220576041f;
@@ -56,20 +59,6 @@ __device__ __forceinline__ int xhalf_max(int x) {
 __device__ __forceinline__ float xhalf_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
   return __int_as_float((int)r[0]) + __int_as_float((int)r[1]);
-}
-
-// S^T tile pair of one epoch: acc[t] = K(keys 32t..32t+31) . Q^T over 128 channels.
-__device__ __forceinline__ void qk_epoch(v16i (&acc)[2], const uint8_t* Kl, const v4i (&qop)[4], int lane) {
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[t][i] = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const v4i a = *reinterpret_cast<const v4i*>(Kl + ((t * 4 + u) * 64 + lane) * 16);
-      acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qop[u], acc[t], 0, 0, 0);
-    }
-  }
 }
 
 // O^T += V^T P^T for one 32-channel tile w.
@@ -103,7 +92,7 @@ __device__ __forceinline__ uint8_t* stage() {
 struct Pipe {
   v16f oacc[4];  // O^T, 32 channels x 32 queries per tile
   v4i qop[4];    // Q operand (this wave's 32 queries)
-  v8i pb_prev;   // E4M3 probabilities of the previous epoch (PV deferred by one step)
+  v8i pb[2];     // E4M3 probabilities of epochs of even / odd stage (PV deferred one step)
   float alpha_prev;  // its rescale factor, applied to O just before its PV is accumulated
   float m, dpart, sig_q;
   const float* ksc;
@@ -134,13 +123,26 @@ __device__ __forceinline__ void issue_tile(const Pipe& c, int e) {
   }
 }
 
-// Online softmax of one epoch for this lane's query (32 of the 64 keys; the other 32 are
-// in lane ^ 32), with the deferred PV MFMAs of the previous epoch interleaved (they do
-// not depend on it).  Updates m and the lane's partial denominator (in units of 448*P),
-// packs the E4M3 probabilities into pb and returns alpha.  TAIL masks keys >= kvalid.
-template <bool TAIL>
-__device__ __forceinline__ float softmax_pv(Pipe& c, const v16i (&acc)[2], float sig, int kvalid, v8i& pb,
-                                            const uint8_t* Vprev) {
+// One S^T tile t of epoch e+1: acc_t = K(keys 32t..32t+31) . Q^T over 128 channels.
+__device__ __forceinline__ void qk_tile(v16i& acc_t, const uint8_t* Kl, const v4i (&qop)[4], int lane, int t) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc_t[i] = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const v4i a = *reinterpret_cast<const v4i*>(Kl + ((t * 4 + u) * 64 + lane) * 16);
+    acc_t = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qop[u], acc_t, 0, 0, 0);
+  }
+}
+
+// Online softmax of epoch e for this lane's query (32 of the 64 keys; the other 32 are in
+// lane ^ 32).  Interleaved with it, on the matrix cores: PV of epoch e-1 (one 32-channel
+// tile per chunk of 8 probabilities) and, once a score tile has been consumed, QK of
+// epoch e+1 into the same registers (NEXT).  Updates m and the lane's partial
+// denominator (in units of 448*P), packs the E4M3 probabilities into pb and returns alpha.
+// TAIL masks keys >= kvalid.
+template <bool TAIL, bool NEXT>
+__device__ __forceinline__ float softmax_pv(Pipe& c, v16i (&acc)[2], float sig, int kvalid, v8i& pb,
+                                            const v8i& pb_prev, const uint8_t* Vprev, const uint8_t* Knext) {
   const int g = c.g;
   int mx4[4];
 #pragma unroll
@@ -162,11 +164,16 @@ __device__ __forceinline__ float softmax_pv(Pipe& c, const v16i (&acc)[2], float
   const float mm = m_new - kLog2_448;
   float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {  // chunk w: 8 probabilities, next to PV tile w of epoch e-1
-    pv_tile(c.oacc[w], Vprev, c.pb_prev, c.lane, w);
+  for (int w = 0; w < 4; ++w) {  // chunk w: 8 probabilities of score tile t = w/2
+    // Keep each chunk's MFMAs among its own exponentials: left alone, the scheduler hoists
+    // the (register-independent) QK MFMAs of epoch e+1 above the softmax, which both
+    // blocks this wave's VALU issue behind them and doubles the live score registers.
+    __builtin_amdgcn_sched_barrier(0);
+    pv_tile(c.oacc[w], Vprev, pb_prev, c.lane, w);
+    const int t = w >> 1;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const int t = w >> 1, q4 = 2 * (w & 1) + h2;
+      const int q4 = 2 * (w & 1) + h2;
       float pv[4];
 #pragma unroll
       for (int r3 = 0; r3 < 4; ++r3) {
@@ -175,11 +182,16 @@ __device__ __forceinline__ float softmax_pv(Pipe& c, const v16i (&acc)[2], float
         pv[r3] = __builtin_amdgcn_exp2f(arg);  // 448 * P
         ps[r3] += pv[r3];
       }
-      int w01 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+      int old;  // both halves of the word are written below
+      int w01 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], old, false);
       w01 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w01, true);
       pb[4 * t + q4] = w01;
     }
+    if constexpr (NEXT) {
+      if (w & 1) qk_tile(acc[t], Knext, c.qop, c.lane, t);  // score tile t is consumed
+    }
   }
+  __builtin_amdgcn_sched_barrier(0);
   c.dpart = c.dpart * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
   c.m = m_new;
   return alpha;
@@ -197,20 +209,18 @@ __device__ __forceinline__ void rescale(Pipe& c) {
   }
 }
 
-// Pipeline step for epoch e held in stage ST: wait for tile e, start tile e+2, then
-// (active waves) QK(e), the O rescale by alpha(e-1) while those MFMAs run, and the softmax
-// of e interleaved with PV(e-1).  LAST marks the final epoch (no tile e+1 in flight; TAIL
-// masks its keys), which also accumulates its own PV.
+// Pipeline step for epoch e held in stage ST.  Its scores are already in acc (QK issued
+// during the previous step).  Wait for tile e+1, start tile e+2, then (active waves)
+// rescale O by alpha(e-1) and run the softmax of e with PV(e-1) and QK(e+1) interleaved.
+// LAST marks the final epoch (TAIL masks its keys), which also accumulates its own PV.
 template <int ST, bool LAST, bool TAIL, bool DUMP>
-__device__ __forceinline__ void pipe_step(Pipe& c, int e, int kvalid, const Dump& dump) {
-  constexpr int ST_PREV = (ST + kStages - 1) % kStages, ST_NEXT2 = (ST + 2) % kStages;
-  if constexpr (LAST) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerThread) : "memory");  // tile e+1 may fly
-  __syncthreads();  // tile e visible to every wave; every wave is done with step e-1
+__device__ __forceinline__ void pipe_step(Pipe& c, int e, int kvalid, const Dump& dump, v16i (&acc)[2]) {
+  constexpr int ST_PREV = (ST + kStages - 1) % kStages, ST_NEXT = (ST + 1) % kStages,
+                ST_NEXT2 = (ST + 2) % kStages;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile e+1 (in flight since step e-1)
+  __syncthreads();  // tile e+1 visible to every wave; every wave is done with step e-1
   if (e + 2 < c.nkb) issue_tile<ST_NEXT2>(c, e + 2);
   if (!c.active) return;
-  v16i acc[2];
-  qk_epoch(acc, stage<ST>(), c.qop, c.lane);
   rescale(c);  // O = RO(e-2) * alpha(e-1), so PV(e-1) below completes RO(e-1)
   const float sig = c.sig_q * c.ksc[e];  // fl32(fl32(q_scale * c) * k_scale)
   if constexpr (DUMP) {
@@ -228,24 +238,23 @@ __device__ __forceinline__ void pipe_step(Pipe& c, int e, int kvalid, const Dump
         }
     }
   }
-  v8i pb;
-  c.alpha_prev = softmax_pv<TAIL>(c, acc, sig, kvalid, pb, stage<ST_PREV>() + kTileBytes);
-  c.pb_prev = pb;
+  c.alpha_prev = softmax_pv<TAIL, !LAST>(c, acc, sig, kvalid, c.pb[ST & 1], c.pb[(ST + 1) & 1],
+                                         stage<ST_PREV>() + kTileBytes, stage<ST_NEXT>());
   if constexpr (LAST) {
     rescale(c);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) pv_tile(c.oacc[w], stage<ST>() + kTileBytes, pb, c.lane, w);
+    for (int w = 0; w < 4; ++w) pv_tile(c.oacc[w], stage<ST>() + kTileBytes, c.pb[ST & 1], c.lane, w);
   }
 }
 
 template <int ST, bool DUMP>
-__device__ __forceinline__ void last_step(Pipe& c, int e, int kvalid, const Dump& dump) {
-  if (kvalid == kBlk) pipe_step<ST, true, false, DUMP>(c, e, kBlk, dump);
-  else pipe_step<ST, true, true, DUMP>(c, e, kvalid, dump);
+__device__ __forceinline__ void last_step(Pipe& c, int e, int kvalid, const Dump& dump, v16i (&acc)[2]) {
+  if (kvalid == kBlk) pipe_step<ST, true, false, DUMP>(c, e, kBlk, dump, acc);
+  else pipe_step<ST, true, true, DUMP>(c, e, kvalid, dump, acc);
 }
 
 template <bool DUMP>
-__global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnParams p) {
   __shared__ float s_vscale[kD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -302,7 +311,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) c.oacc[w][i] = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c.pb_prev[i] = 0;
+  for (int i = 0; i < 8; ++i) c.pb[0][i] = c.pb[1][i] = 0;
   if (c.active) {
     const int8_t* qt_ptr = p.q8 + ((int64_t)h * p.qblk_cap + qi.blk0 + qb) * kTileBytes;
 #pragma unroll
@@ -326,32 +335,43 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
   dump.on = DUMP && s == p.dump_seg && h == p.dump_head;
 
   // ---------------------------------------------------------------- epoch pipeline
-  // Epoch e lives in stage e % 4; step e reads its K tile and the V tile of epoch e-1,
-  // while tile e+2 streams in.  The V half of stage 3 starts as zeros: step 0's deferred
-  // PV multiplies it by all-zero probabilities.
-  reinterpret_cast<v4i*>(stage<3>() + kTileBytes)[tid] = v4i{0, 0, 0, 0};
+  // Epoch e lives in stage e % 4.  Step e reads the V tile of epoch e-1 and the K tile of
+  // epoch e+1 while tile e+2 streams in.  The V half of stage 3 starts as zeros: step 0's
+  // deferred PV multiplies it by all-zero probabilities.
+#pragma unroll
+  for (int i = tid; i < kTileBytes / 16; i += kWaves * 64)
+    reinterpret_cast<v4i*>(stage<3>() + kTileBytes)[i] = v4i{0, 0, 0, 0};
+  v16i acc[2];
   if (nkb > 0) issue_tile<0>(c, 0);
-  if (nkb > 1) issue_tile<1>(c, 1);
+  if (nkb > 1) {
+    issue_tile<1>(c, 1);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerThread) : "memory");  // tile 0 landed
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();  // tile 0, the zeroed stage and s_vscale visible
+  if (c.active && nkb > 0) {
+    qk_tile(acc[0], stage<0>(), c.qop, lane, 0);
+    qk_tile(acc[1], stage<0>(), c.qop, lane, 1);
+  }
   const int nfull = nkb - 1;  // epochs before the last one
   int e = 0;
   for (; e + 4 <= nfull; e += 4) {
-    pipe_step<0, false, false, DUMP>(c, e, kBlk, dump);
-    pipe_step<1, false, false, DUMP>(c, e + 1, kBlk, dump);
-    pipe_step<2, false, false, DUMP>(c, e + 2, kBlk, dump);
-    pipe_step<3, false, false, DUMP>(c, e + 3, kBlk, dump);
+    pipe_step<0, false, false, DUMP>(c, e, kBlk, dump, acc);
+    pipe_step<1, false, false, DUMP>(c, e + 1, kBlk, dump, acc);
+    pipe_step<2, false, false, DUMP>(c, e + 2, kBlk, dump, acc);
+    pipe_step<3, false, false, DUMP>(c, e + 3, kBlk, dump, acc);
   }
-  if (e < nfull) pipe_step<0, false, false, DUMP>(c, e, kBlk, dump);
-  if (e + 1 < nfull) pipe_step<1, false, false, DUMP>(c, e + 1, kBlk, dump);
-  if (e + 2 < nfull) pipe_step<2, false, false, DUMP>(c, e + 2, kBlk, dump);
+  if (e < nfull) pipe_step<0, false, false, DUMP>(c, e, kBlk, dump, acc);
+  if (e + 1 < nfull) pipe_step<1, false, false, DUMP>(c, e + 1, kBlk, dump, acc);
+  if (e + 2 < nfull) pipe_step<2, false, false, DUMP>(c, e + 2, kBlk, dump, acc);
   if (nkb > 0) {
     switch (nfull & 3) {
-      case 0: last_step<0, DUMP>(c, nfull, last_valid, dump); break;
-      case 1: last_step<1, DUMP>(c, nfull, last_valid, dump); break;
-      case 2: last_step<2, DUMP>(c, nfull, last_valid, dump); break;
-      default: last_step<3, DUMP>(c, nfull, last_valid, dump); break;
+      case 0: last_step<0, DUMP>(c, nfull, last_valid, dump, acc); break;
+      case 1: last_step<1, DUMP>(c, nfull, last_valid, dump, acc); break;
+      case 2: last_step<2, DUMP>(c, nfull, last_valid, dump, acc); break;
+      default: last_step<3, DUMP>(c, nfull, last_valid, dump, acc); break;
     }
-  } else {
-    __syncthreads();  // s_vscale visible
   }
 
   // ---------------------------------------------------------------- epilogue
