@@ -13,7 +13,7 @@ SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.hip", "quant.hip", "attn
 FLAGS = [
     "-O3",
     "--offload-arch=gfx950",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-shared",
     "-fvisibility=hidden",

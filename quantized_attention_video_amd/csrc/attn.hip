@@ -9,10 +9,11 @@
 // softmax occupies the vector pipes).  The pages' GB10 kernel is warp-specialised with
 // mbarriers; this one is designed for CDNA4 instead:
 //
-//  * One workgroup = 4 waves = 128 queries of one (segment, head); each wave owns 32
-//    queries and stays under 256 VGPRs, so two workgroups share a CU and every SIMD runs
-//    two waves of different workgroups.  Their barriers are independent, so one wave's
-//    softmax (VALU) overlaps the other's MFMAs instead of both stalling in step.
+//  * One workgroup = 12 waves = 384 queries of one (segment, head), one workgroup per CU,
+//    three waves per SIMD.  A single wave issues a VALU instruction only every ~7 cycles
+//    on gfx950, and the VALU (softmax) is the binding unit, so the SIMD needs three
+//    resident waves; each wave owns 32 queries and keeps its Q operand in LDS to stay
+//    within 168 VGPRs.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_i32_32x32x32_i8: each lane
 //    owns one query column and 32 of the epoch's 64 keys, so the row max and row sum are
 //    in-lane plus one v_permlane32_swap between the two half-waves.
@@ -40,12 +41,17 @@
 #include <limits.h>
 #include <math.h>
 
+#include <utility>
+
 #include "device_common.h"
 #include "launch.h"
 
 namespace sattn {
 
-constexpr int kWaves = 4;                  // waves per workgroup (two workgroups per CU)
+constexpr int kWaves = 4;                  // waves per workgroup: two workgroups per CU
+constexpr int kLoaderWaves = 4;            // waves that stream the K/V tiles
+constexpr bool kQInLds = kWaves > 4;       // Q operand in LDS (frees 16 VGPRs) or in registers
+constexpr int kWavesPerSimd = kWaves > 4 ? kWaves / 4 : 2;
 constexpr int kQPerWG = kWaves * 32;       // queries per workgroup
 constexpr int kQBlocksPerWG = kWaves / 2;  // 64-query blocks per workgroup
 constexpr float kLog2_448 = 8.8073549220576041f;
@@ -61,23 +67,41 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __int_as_float((int)r[0]) + __int_as_float((int)r[1]);
 }
 
-// O^T += V^T P^T for one 32-channel tile w.
-__device__ __forceinline__ void pv_tile(v16f& o, const uint8_t* Vl, const v8i& pb, int lane, int w) {
+// LDS operands of one PV tile w (V^T rows 32w..32w+31, 64 keys) and one QK step u of
+// score tile t (K rows 32t.., channels 64g + 16u ..).
+__device__ __forceinline__ v8i load_v(const uint8_t* Vl, int lane, int w) {
   const v4i lo = *reinterpret_cast<const v4i*>(Vl + ((w * 2 + 0) * 64 + lane) * 16);
   const v4i hi = *reinterpret_cast<const v4i*>(Vl + ((w * 2 + 1) * 64 + lane) * 16);
-  const v8i a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ v4i load_k(const uint8_t* Kl, int lane, int t, int u) {
+  return *reinterpret_cast<const v4i*>(Kl + ((t * 4 + u) * 64 + lane) * 16);
+}
+__device__ __forceinline__ void pv_mfma(v16f& o, const v8i& a, const v8i& pb) {
   o = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, o, 0, 0, 0, 0, 0, 0);
 }
+// O^T += V^T P^T for one 32-channel tile w (operands read here).
+__device__ __forceinline__ void pv_tile(v16f& o, const uint8_t* Vl, const v8i& pb, int lane, int w) {
+  pv_mfma(o, load_v(Vl, lane, w), pb);
+}
 
-// K/V tiles of four consecutive epochs live in four separate LDS arrays, so that the
+// The K/V tiles of consecutive epochs live in kStages separate LDS arrays, so that the
 // compiler can tell an LDS-DMA write into one stage from reads of another (one shared
-// array indexed at run time makes it wait for every DMA before any LDS read).
+// array indexed at run time makes it wait for every DMA before any LDS read).  Epoch e
+// uses stage e % kStages; tile e + kPrefetch is requested while epoch e is processed.
+constexpr int kStages = 4;
+constexpr int kPrefetch = kStages - 2;  // stages e-1 (V), e+1 (K) are in use at step e
+static_assert(kStages >= 3 && kStages <= 8, "stages");
 __shared__ __attribute__((aligned(16))) uint8_t g_stage0[2 * kTileBytes];
 __shared__ __attribute__((aligned(16))) uint8_t g_stage1[2 * kTileBytes];
 __shared__ __attribute__((aligned(16))) uint8_t g_stage2[2 * kTileBytes];
 __shared__ __attribute__((aligned(16))) uint8_t g_stage3[2 * kTileBytes];
-constexpr int kStages = 4;
-constexpr int kLoadsPerThread = 1024 / (kWaves * 64);
+__shared__ __attribute__((aligned(16))) uint8_t g_stage4[2 * kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_stage5[2 * kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_stage6[2 * kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_stage7[2 * kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_qop[kQInLds ? kWaves : 1][4096];  // Q operands
+constexpr int kLoadsPerThread = 1024 / (kLoaderWaves * 64);
 
 template <int ST>
 __device__ __forceinline__ uint8_t* stage() {
@@ -85,17 +109,25 @@ __device__ __forceinline__ uint8_t* stage() {
   if constexpr (ST == 0) return g_stage0;
   if constexpr (ST == 1) return g_stage1;
   if constexpr (ST == 2) return g_stage2;
-  return g_stage3;
+  if constexpr (ST == 3) return g_stage3;
+  if constexpr (ST == 4) return g_stage4;
+  if constexpr (ST == 5) return g_stage5;
+  if constexpr (ST == 6) return g_stage6;
+  return g_stage7;
 }
 
 // Per-wave state of the epoch pipeline.
+typedef __attribute__((address_space(4))) const float const_f32;
+
 struct Pipe {
   v16f oacc[4];  // O^T, 32 channels x 32 queries per tile
-  v4i qop[4];    // Q operand (this wave's 32 queries)
+  v4i qop[4];            // this wave's Q operand (register copy)
+  const uint8_t* qlds;   // this wave's Q operand in LDS
   v8i pb[2];     // E4M3 probabilities of epochs of even / odd stage (PV deferred one step)
   float alpha_prev;  // its rescale factor, applied to O just before its PV is accumulated
   float m, dpart, sig_q;
-  const float* ksc;
+  const_f32* ksc;   // K block scales, read through the scalar cache
+  float ks_next;    // scale of the next epoch, loaded one step ahead
   const uint8_t *kg, *vg;
   int lane, wave, g, nkb;
   bool active;
@@ -113,37 +145,57 @@ struct Dump {
 // j covers chunks j*512 + w*64 + lane, which lie in one tile (wave-uniform LDS base).
 template <int ST>
 __device__ __forceinline__ void issue_tile(const Pipe& c, int e) {
+  if (c.wave >= kLoaderWaves) return;
 #pragma unroll
   for (int j = 0; j < kLoadsPerThread; ++j) {
-    const int c0 = j * kWaves * 64 + c.wave * 64;
+    const int c0 = j * kLoaderWaves * 64 + c.wave * 64;  // wave-uniform
     const int which = c0 >> 9, cw = c0 & 511;
-    const uint8_t* src = (which ? c.vg : c.kg) + (int64_t)e * kTileBytes + (int64_t)(cw + c.lane) * 16;
-    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(stage<ST>() + which * kTileBytes + cw * 16),
-                                     16, 0, 0);
+    const uint8_t* base = (which ? c.vg : c.kg) + (int64_t)e * kTileBytes + cw * 16;  // uniform
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(base + c.lane * 16),
+                                     (lds_void_t*)(stage<ST>() + which * kTileBytes + cw * 16), 16, 0, 0);
   }
 }
 
-// One S^T tile t of epoch e+1: acc_t = K(keys 32t..32t+31) . Q^T over 128 channels.
-__device__ __forceinline__ void qk_tile(v16i& acc_t, const uint8_t* Kl, const v4i (&qop)[4], int lane, int t) {
+// One S^T tile t: acc_t = K(keys 32t..32t+31) . Q^T over 128 channels, with the K operands
+// already in registers.  The wave's Q operand is either in registers (qop) or in LDS at
+// Ql (four 1 KiB lane-ordered chunks).
+__device__ __forceinline__ void qk_mfma(v16i& acc_t, const v4i (&ka)[4], const v4i (&qop)[4], const uint8_t* Ql,
+                                        int lane) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc_t[i] = 0;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const v4i a = *reinterpret_cast<const v4i*>(Kl + ((t * 4 + u) * 64 + lane) * 16);
-    acc_t = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qop[u], acc_t, 0, 0, 0);
+    v4i b;
+    if constexpr (kQInLds) b = *reinterpret_cast<const v4i*>(Ql + (u * 64 + lane) * 16);
+    else b = qop[u];
+    acc_t = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[u], b, acc_t, 0, 0, 0);
   }
+}
+__device__ __forceinline__ void qk_tile(v16i& acc_t, const uint8_t* Kl, const v4i (&qop)[4], const uint8_t* Ql,
+                                        int lane, int t) {
+  v4i ka[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) ka[u] = load_k(Kl, lane, t, u);
+  qk_mfma(acc_t, ka, qop, Ql, lane);
 }
 
 // Online softmax of epoch e for this lane's query (32 of the 64 keys; the other 32 are in
-// lane ^ 32).  Interleaved with it, on the matrix cores: PV of epoch e-1 (one 32-channel
-// tile per chunk of 8 probabilities) and, once a score tile has been consumed, QK of
-// epoch e+1 into the same registers (NEXT).  Updates m and the lane's partial
-// denominator (in units of 448*P), packs the E4M3 probabilities into pb and returns alpha.
-// TAIL masks keys >= kvalid.
+// lane ^ 32).  Interleaved with it, on the matrix cores: PV of epoch e-1 and, once a
+// score tile has been consumed, QK of epoch e+1 into the same registers (NEXT).  Updates
+// m and the lane's partial denominator (in units of 448*P), packs the E4M3 probabilities
+// into pb and returns alpha.  TAIL masks keys >= kvalid.
+//
+// The step is cut into four chunks of 8 probabilities (scheduling barriers between them).
+// Each chunk issues about 128 cycles of MFMA work whose LDS operands were read one chunk
+// earlier, so in-order issue never waits on LDS, then its VALU work: chunk 0 PV(e-1)
+// tiles 0,1; chunk 1 tiles 2,3 (the previous probabilities die half-way); chunk 2
+// QK(e+1) score tile 0 (consumed by chunks 0-1); score tile 1 follows chunk 3.
 template <bool TAIL, bool NEXT>
 __device__ __forceinline__ float softmax_pv(Pipe& c, v16i (&acc)[2], float sig, int kvalid, v8i& pb,
                                             const v8i& pb_prev, const uint8_t* Vprev, const uint8_t* Knext) {
   const int g = c.g;
+  v8i va = load_v(Vprev, c.lane, 0), vb = load_v(Vprev, c.lane, 1);
+  __builtin_amdgcn_sched_barrier(0);  // the reads go out first; the row max hides them
   int mx4[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {  // four independent max chains of 8 (t = q/2, rows 8(q%2)..)
@@ -163,13 +215,26 @@ __device__ __forceinline__ float softmax_pv(Pipe& c, v16i (&acc)[2], float sig, 
   const float alpha = __builtin_amdgcn_exp2f(c.m - m_new);  // 0 on the first epoch
   const float mm = m_new - kLog2_448;
   float ps[4] = {0.f, 0.f, 0.f, 0.f};
+  v4i ka[4];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {  // chunk w: 8 probabilities of score tile t = w/2
-    // Keep each chunk's MFMAs among its own exponentials: left alone, the scheduler hoists
-    // the (register-independent) QK MFMAs of epoch e+1 above the softmax, which both
-    // blocks this wave's VALU issue behind them and doubles the live score registers.
+  for (int w = 0; w < 4; ++w) {
     __builtin_amdgcn_sched_barrier(0);
-    pv_tile(c.oacc[w], Vprev, pb_prev, c.lane, w);
+    if (w < 2) {  // PV(e-1): operands read one chunk ago
+      pv_mfma(c.oacc[2 * w], va, pb_prev);
+      pv_mfma(c.oacc[2 * w + 1], vb, pb_prev);
+      if (w == 0) {
+        va = load_v(Vprev, c.lane, 2);
+        vb = load_v(Vprev, c.lane, 3);
+      }
+    }
+    if constexpr (NEXT) {
+      if (w == 2) qk_mfma(acc[0], ka, c.qop, c.qlds, c.lane);  // operands read in chunk 1
+      if (w == 1 || w == 2) {                                   // operands of score tile w-1
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ka[u] = load_k(Knext, c.lane, w - 1, u);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // MFMA issue and operand reads ahead of the VALU
     const int t = w >> 1;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -182,16 +247,17 @@ __device__ __forceinline__ float softmax_pv(Pipe& c, v16i (&acc)[2], float sig, 
         pv[r3] = __builtin_amdgcn_exp2f(arg);  // 448 * P
         ps[r3] += pv[r3];
       }
-      int old;  // both halves of the word are written below
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wuninitialized"
+      int old;  // both halves of the word are written below; no register needs zeroing
       int w01 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], old, false);
+#pragma clang diagnostic pop
       w01 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w01, true);
       pb[4 * t + q4] = w01;
     }
-    if constexpr (NEXT) {
-      if (w & 1) qk_tile(acc[t], Knext, c.qop, c.lane, t);  // score tile t is consumed
-    }
   }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (NEXT) qk_mfma(acc[1], ka, c.qop, c.qlds, c.lane);
   c.dpart = c.dpart * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
   c.m = m_new;
   return alpha;
@@ -216,13 +282,16 @@ __device__ __forceinline__ void rescale(Pipe& c) {
 template <int ST, bool LAST, bool TAIL, bool DUMP>
 __device__ __forceinline__ void pipe_step(Pipe& c, int e, int kvalid, const Dump& dump, v16i (&acc)[2]) {
   constexpr int ST_PREV = (ST + kStages - 1) % kStages, ST_NEXT = (ST + 1) % kStages,
-                ST_NEXT2 = (ST + 2) % kStages;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile e+1 (in flight since step e-1)
+                ST_PF = (ST + kPrefetch) % kStages;
+  // Tile e+1 must have landed; tiles e+2 .. e+kPrefetch-1 may still be in flight.
+  if (e + kPrefetch - 1 < c.nkb) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kPrefetch - 2) * kLoadsPerThread) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();  // tile e+1 visible to every wave; every wave is done with step e-1
-  if (e + 2 < c.nkb) issue_tile<ST_NEXT2>(c, e + 2);
+  if (e + kPrefetch < c.nkb) issue_tile<ST_PF>(c, e + kPrefetch);
   if (!c.active) return;
   rescale(c);  // O = RO(e-2) * alpha(e-1), so PV(e-1) below completes RO(e-1)
-  const float sig = c.sig_q * c.ksc[e];  // fl32(fl32(q_scale * c) * k_scale)
+  const float sig = c.sig_q * c.ks_next;  // fl32(fl32(q_scale * c) * k_scale)
+  if (e + 1 < c.nkb) c.ks_next = c.ksc[e + 1];
   if constexpr (DUMP) {
     if (dump.on && dump.row < dump.len_q) {
 #pragma unroll
@@ -253,10 +322,30 @@ __device__ __forceinline__ void last_step(Pipe& c, int e, int kvalid, const Dump
   else pipe_step<ST, true, true, DUMP>(c, e, kvalid, dump, acc);
 }
 
+// kStages full steps e .. e+kStages-1 (stages 0 .. kStages-1).
+template <bool DUMP, int... STs>
+__device__ __forceinline__ void steps_all(Pipe& c, int e, const Dump& dump, v16i (&acc)[2],
+                                          std::integer_sequence<int, STs...>) {
+  (pipe_step<STs, false, false, DUMP>(c, e + STs, kBlk, dump, acc), ...);
+}
+// The remaining full steps e + ST < nfull (e a multiple of kStages).
+template <bool DUMP, int... STs>
+__device__ __forceinline__ void steps_rest(Pipe& c, int e, int nfull, const Dump& dump, v16i (&acc)[2],
+                                           std::integer_sequence<int, STs...>) {
+  ((e + STs < nfull ? pipe_step<STs, false, false, DUMP>(c, e + STs, kBlk, dump, acc) : void()), ...);
+}
+// The last epoch nfull, in stage nfull % kStages.
+template <bool DUMP, int... STs>
+__device__ __forceinline__ void step_last(Pipe& c, int nfull, int kvalid, const Dump& dump, v16i (&acc)[2],
+                                          std::integer_sequence<int, STs...>) {
+  const int st = nfull % kStages;
+  ((st == STs ? last_step<STs, DUMP>(c, nfull, kvalid, dump, acc) : void()), ...);
+}
+
 template <bool DUMP>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnParams p) {
-  __shared__ float s_vscale[kD];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void attn_fwd_kernel(AttnParams p) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level addressing in SGPRs
 
   // ---------------------------------------------------------------- work item
   const int xcd = blockIdx.x & 7;
@@ -294,7 +383,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const int64_t qb = qt * kQBlocksPerWG + (wave >> 1);  // this wave's 64-query block
   const int hq = wave & 1;                              // and which 32 of its queries
 
-  if (tid < kD) s_vscale[tid] = p.v_scale[((int64_t)s * p.H + h) * kD + tid];
 
   Pipe c;
   c.lane = lane;
@@ -312,19 +400,26 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     for (int i = 0; i < 16; ++i) c.oacc[w][i] = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) c.pb[0][i] = c.pb[1][i] = 0;
+  c.qlds = g_qop[kQInLds ? wave : 0];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) c.qop[u] = v4i{0, 0, 0, 0};
   if (c.active) {
     const int8_t* qt_ptr = p.q8 + ((int64_t)h * p.qblk_cap + qi.blk0 + qb) * kTileBytes;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) c.qop[u] = *reinterpret_cast<const v4i*>(qt_ptr + ((hq * 4 + u) * 64 + lane) * 16);
+    for (int u = 0; u < 4; ++u) {
+      const int8_t* src = qt_ptr + ((hq * 4 + u) * 64 + lane) * 16;
+      if constexpr (kQInLds)  // streamed into LDS; landed by the first barrier
+        __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(g_qop[wave] + u * 1024), 16, 0, 0);
+      else
+        c.qop[u] = *reinterpret_cast<const v4i*>(src);
+    }
     c.sig_q = p.q_scale[(int64_t)h * p.qblk_cap + qi.blk0 + qb] * p.c32;  // fl32(q_scale * c)
-  } else {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) c.qop[u] = v4i{0, 0, 0, 0};
   }
   const int64_t ktile0 = (int64_t)h * p.kblk_cap + ki.blk0;
   c.kg = reinterpret_cast<const uint8_t*>(p.k8) + ktile0 * kTileBytes;
   c.vg = p.v8 + ktile0 * kTileBytes;
-  c.ksc = p.k_scale + ktile0;
+  c.ksc = (const_f32*)(p.k_scale + ktile0);
+  c.ks_next = nkb > 0 ? c.ksc[0] : 0.f;
 
   Dump dump;
   dump.acc = p.dump_acc;
@@ -335,44 +430,30 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   dump.on = DUMP && s == p.dump_seg && h == p.dump_head;
 
   // ---------------------------------------------------------------- epoch pipeline
-  // Epoch e lives in stage e % 4.  Step e reads the V tile of epoch e-1 and the K tile of
-  // epoch e+1 while tile e+2 streams in.  The V half of stage 3 starts as zeros: step 0's
-  // deferred PV multiplies it by all-zero probabilities.
+  // Epoch e lives in stage e % kStages.  Step e reads the V tile of epoch e-1 and the K
+  // tile of epoch e+1 while tile e+kPrefetch streams in.  The V half of the last stage
+  // starts as zeros: step 0's deferred PV multiplies it by all-zero probabilities.
 #pragma unroll
   for (int i = tid; i < kTileBytes / 16; i += kWaves * 64)
-    reinterpret_cast<v4i*>(stage<3>() + kTileBytes)[i] = v4i{0, 0, 0, 0};
+    reinterpret_cast<v4i*>(stage<kStages - 1>() + kTileBytes)[i] = v4i{0, 0, 0, 0};
   v16i acc[2];
-  if (nkb > 0) issue_tile<0>(c, 0);
-  if (nkb > 1) {
-    issue_tile<1>(c, 1);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerThread) : "memory");  // tile 0 landed
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  __syncthreads();  // tile 0, the zeroed stage and s_vscale visible
+  // prologue: tiles 0 .. kPrefetch-1 into stages 0 .. kPrefetch-1 (never the zeroed one)
+  [&]<int... STs>(std::integer_sequence<int, STs...>) {
+    ((STs < nkb ? issue_tile<STs>(c, STs) : void()), ...);
+  }(std::make_integer_sequence<int, kPrefetch>{});
+  if (kPrefetch - 1 < nkb) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kPrefetch - 1) * kLoadsPerThread) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // Q, tile 0 and the zeroed stage visible
   if (c.active && nkb > 0) {
-    qk_tile(acc[0], stage<0>(), c.qop, lane, 0);
-    qk_tile(acc[1], stage<0>(), c.qop, lane, 1);
+    qk_tile(acc[0], stage<0>(), c.qop, c.qlds, lane, 0);
+    qk_tile(acc[1], stage<0>(), c.qop, c.qlds, lane, 1);
   }
   const int nfull = nkb - 1;  // epochs before the last one
   int e = 0;
-  for (; e + 4 <= nfull; e += 4) {
-    pipe_step<0, false, false, DUMP>(c, e, kBlk, dump, acc);
-    pipe_step<1, false, false, DUMP>(c, e + 1, kBlk, dump, acc);
-    pipe_step<2, false, false, DUMP>(c, e + 2, kBlk, dump, acc);
-    pipe_step<3, false, false, DUMP>(c, e + 3, kBlk, dump, acc);
-  }
-  if (e < nfull) pipe_step<0, false, false, DUMP>(c, e, kBlk, dump, acc);
-  if (e + 1 < nfull) pipe_step<1, false, false, DUMP>(c, e + 1, kBlk, dump, acc);
-  if (e + 2 < nfull) pipe_step<2, false, false, DUMP>(c, e + 2, kBlk, dump, acc);
-  if (nkb > 0) {
-    switch (nfull & 3) {
-      case 0: last_step<0, DUMP>(c, nfull, last_valid, dump, acc); break;
-      case 1: last_step<1, DUMP>(c, nfull, last_valid, dump, acc); break;
-      case 2: last_step<2, DUMP>(c, nfull, last_valid, dump, acc); break;
-      default: last_step<3, DUMP>(c, nfull, last_valid, dump, acc); break;
-    }
-  }
+  for (; e + kStages <= nfull; e += kStages)
+    steps_all<DUMP>(c, e, dump, acc, std::make_integer_sequence<int, kStages>{});
+  steps_rest<DUMP>(c, e, nfull, dump, acc, std::make_integer_sequence<int, kStages - 1>{});
+  if (nkb > 0) step_last<DUMP>(c, nfull, last_valid, dump, acc, std::make_integer_sequence<int, kStages>{});
 
   // ---------------------------------------------------------------- epilogue
   if (!c.active) return;
@@ -381,14 +462,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const int64_t row = qb * kBlk + hq * 32 + (lane & 31);
   if (row >= qi.len) return;
   uint16_t* orow = p.o + qi.elem_base + row * p.o_st + (int64_t)h * p.o_sh;
+  const float* vsc = p.v_scale + ((int64_t)s * p.H + h) * kD;
 #pragma unroll
   for (int w = 0; w < 4; ++w)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int c0 = 32 * w + 8 * q4 + 4 * c.g;
+      const float4 vs = *reinterpret_cast<const float4*>(vsc + c0);
+      const float vsa[4] = {vs.x, vs.y, vs.z, vs.w};
       uint32_t b[4];
 #pragma unroll
-      for (int r3 = 0; r3 < 4; ++r3) b[r3] = f32_to_bf16_bits((c.oacc[w][4 * q4 + r3] * inv) * s_vscale[c0 + r3]);
+      for (int r3 = 0; r3 < 4; ++r3) b[r3] = f32_to_bf16_bits((c.oacc[w][4 * q4 + r3] * inv) * vsa[r3]);
       *reinterpret_cast<uint2*>(orow + c0) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
     }
 }
