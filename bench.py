@@ -50,34 +50,41 @@ def measured_traffic(workload):
         return None
 
 
-def cpu_baseline(w, inp, heads=4, rows=128):
-    """Time the oracle on `heads` heads (full-length quantization) and `rows` query rows of
-    attention per head, then extrapolate linearly to the whole step."""
+def _head_slice(seg, n):
+    """The first n heads of one segment of the oracle's quantized output."""
+    return {k: (v[:, :n] if k in ("q8", "k8", "v8", "v8val") else v[:n]) for k, v in seg.items()}
+
+
+def cpu_baseline(w, inp, att_heads=8, rows=1024):
+    """Time the oracle on a bounded sample of the step: the quantization of all heads over
+    all tokens, and attention for `rows` query rows (half from each end) of `att_heads`
+    heads against all keys; the attention time is extrapolated linearly to every row and
+    head."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import sattn as O
     from quantized_attention_video_amd import workloads as W
 
-    q, k, v = (W.packed_float64(inp[n][:, :, :heads]) for n in "qkv")
+    q, k, v = (W.packed_float64(inp[n]) for n in "qkv")
     t0 = time.perf_counter()
     quant = O.quantize(q, k, v, inp["cu_q"], inp["cu_k"])
     t1 = time.perf_counter()
     L = w.Lq
     sel = np.concatenate([np.arange(0, rows // 2), np.arange(L - rows // 2, L)])
-    O.attention(quant, w.sm_scale, rows={0: sel})
+    O.attention([_head_slice(seg, att_heads) for seg in quant], w.sm_scale, rows={0: sel})
     t2 = time.perf_counter()
-    scale_h = w.H / heads
-    est = (t1 - t0) * scale_h + (t2 - t1) * scale_h * (L / rows)
+    est = (t1 - t0) + (t2 - t1) * (w.H / att_heads) * (L / rows)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {
         "value": w.ops() / est / 1e12,
         "unit": "TOPS",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"FP64 oracle: quantization of {heads}/{w.H} heads over all {L} tokens "
-                   f"({t1 - t0:.1f} s) + attention for {rows} query rows of those heads against all keys "
-                   f"({t2 - t1:.1f} s); extrapolated linearly to the full step = {est:.0f} s"),
+        "sample": (f"FP64 oracle: quantization of all {w.H} heads over all {L} tokens ({t1 - t0:.1f} s) + "
+                   f"attention for {rows} query rows of {att_heads}/{w.H} heads against all keys "
+                   f"({t2 - t1:.1f} s); attention extrapolated linearly to all rows and heads: "
+                   f"full step = {est:.0f} s"),
         "cpu": _cpu_model(),
     }
 

@@ -9,11 +9,11 @@
 // softmax occupies the vector pipes).  The pages' GB10 kernel is warp-specialised with
 // mbarriers; this one is designed for CDNA4 instead:
 //
-//  * One workgroup = 12 waves = 384 queries of one (segment, head), one workgroup per CU,
-//    three waves per SIMD.  A single wave issues a VALU instruction only every ~7 cycles
-//    on gfx950, and the VALU (softmax) is the binding unit, so the SIMD needs three
-//    resident waves; each wave owns 32 queries and keeps its Q operand in LDS to stay
-//    within 168 VGPRs.
+//  * One workgroup = 4 waves = 128 queries of one (segment, head); two workgroups share a
+//    CU, so each SIMD runs two waves of up to 256 VGPRs.  Each wave owns 32 queries end to
+//    end: Q operand, scores, running max and denominator, and the FP32 O accumulators.
+//    The softmax's vector work (about five VALU instructions per score, two of them
+//    transcendental-rate) is the binding resource; the MFMA work runs beside it.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_i32_32x32x32_i8: each lane
 //    owns one query column and 32 of the epoch's 64 keys, so the row max and row sum are
 //    in-lane plus one v_permlane32_swap between the two half-waves.
@@ -34,10 +34,10 @@
 //    ALUs work at the same time.
 //  * The O rescale by alpha is skipped when no row of the wave changed its max (alpha is
 //    then exactly 1, so skipping is bit-identical).
-//  * Work items (segment, head, 256-query tile) are ordered so that consecutive
-//    workgroups dispatched to one XCD take the same head and neighbouring query tiles,
-//    so the 32 CUs of an XCD stream the same K/V tiles through their shared L2; packed
-//    batches are ordered longest-first.
+//  * Work items (segment, head, 128-query tile) are ordered so that consecutive
+//    workgroups dispatched to one XCD (workgroup b runs on XCD b mod 8) take the same
+//    head and neighbouring query tiles, so the CUs of an XCD stream the same K/V tiles
+//    through their shared L2; packed batches are ordered longest-first.
 #include <limits.h>
 #include <math.h>
 
