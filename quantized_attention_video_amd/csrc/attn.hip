@@ -26,8 +26,9 @@
 //  * The lane's 32 probabilities are packed with v_cvt_pk_fp8_f32 directly into the B
 //    operand of v_mfma_f32_32x32x64_f8f6f4 (O^T += V^T P^T).  The V tile is stored by the
 //    quantizer with its keys permuted to match, so no probability goes through LDS.
-//  * K and V tiles (8 KiB each per epoch) stream into four LDS stages with
-//    global_load_lds_dwordx4 (no VGPR staging); one barrier per epoch.  Between the
+//  * K and V tiles (8 KiB each per epoch) stream into three-slot LDS rings with
+//    global_load_lds_dwordx4 (no VGPR staging), two epochs ahead of their use; one
+//    barrier per epoch.  Between the
 //    exponentials of epoch e the wave issues the P.V MFMAs of epoch e-1 and, as each
 //    score tile of epoch e is consumed, the QK MFMAs of epoch e+1 into the same
 //    registers: no MFMA result is waited for inside a step, and matrix cores and vector
@@ -85,45 +86,62 @@ __device__ __forceinline__ void pv_tile(v16f& o, const uint8_t* Vl, const v8i& p
   pv_mfma(o, load_v(Vl, lane, w), pb);
 }
 
-// The K/V tiles of consecutive epochs live in kStages separate LDS arrays, so that the
-// compiler can tell an LDS-DMA write into one stage from reads of another (one shared
-// array indexed at run time makes it wait for every DMA before any LDS read).  Epoch e
-// uses stage e % kStages; tile e + kPrefetch is requested while epoch e is processed.
-constexpr int kStages = 4;
-constexpr int kPrefetch = kStages - 2;  // stages e-1 (V), e+1 (K) are in use at step e
-static_assert(kStages >= 3 && kStages <= 8, "stages");
-__shared__ __attribute__((aligned(16))) uint8_t g_stage0[2 * kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_stage1[2 * kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_stage2[2 * kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_stage3[2 * kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_stage4[2 * kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_stage5[2 * kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_stage6[2 * kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_stage7[2 * kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_qop[kQInLds ? kWaves : 1][4096];  // Q operands
-constexpr int kLoadsPerThread = 1024 / (kLoaderWaves * 64);
+// K and V tiles live in two three-slot LDS rings: epoch e's K tile in k slot e % 3, its V
+// tile in v slot e % 3.  Step e reads K(e+1) (QK of the next epoch) and V(e-1) (the
+// deferred PV) and requests K(e+3) and V(e+1), so every tile has two epochs to land.  Each
+// slot is its own array, so every LDS address in the unrolled loop is a constant.
+constexpr int kRing = 3;
+constexpr int kUnroll = 6;  // lcm of the ring length and the probability double buffer
+__shared__ __attribute__((aligned(16))) uint8_t g_k0[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_k1[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_k2[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_v0[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_v1[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_v2[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_qop[kQInLds ? kWaves : 1][kQInLds ? 4096 : 16];  // Q operands
+constexpr int kChunksPerTile = kTileBytes / 16 / (kLoaderWaves * 64);  // per loader lane
+static_assert(kChunksPerTile * kLoaderWaves * 64 * 16 == kTileBytes, "tile split");
 
-template <int ST>
-__device__ __forceinline__ uint8_t* stage() {
-  static_assert(ST >= 0 && ST < kStages, "stage");
-  if constexpr (ST == 0) return g_stage0;
-  if constexpr (ST == 1) return g_stage1;
-  if constexpr (ST == 2) return g_stage2;
-  if constexpr (ST == 3) return g_stage3;
-  if constexpr (ST == 4) return g_stage4;
-  if constexpr (ST == 5) return g_stage5;
-  if constexpr (ST == 6) return g_stage6;
-  return g_stage7;
+template <int I>
+__device__ __forceinline__ uint8_t* kslot() {
+  static_assert(I >= 0 && I < kRing, "slot");
+  if constexpr (I == 0) return g_k0;
+  if constexpr (I == 1) return g_k1;
+  return g_k2;
+}
+template <int I>
+__device__ __forceinline__ uint8_t* vslot() {
+  static_assert(I >= 0 && I < kRing, "slot");
+  if constexpr (I == 0) return g_v0;
+  if constexpr (I == 1) return g_v1;
+  return g_v2;
 }
 
 // Per-wave state of the epoch pipeline.
 typedef __attribute__((address_space(4))) const float const_f32;
 
+// Workgroup barrier without the memory fence of __syncthreads(): that fence makes a wave
+// wait for all of its LDS-DMA requests, which would cap the tile prefetch at one epoch.
+// LDS accesses of this wave are completed here (lgkmcnt(0)); tile requests are waited for
+// with explicit vmcnt counts before it.
+__device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One 16-byte chunk per lane from global memory into LDS (global_load_lds_dwordx4; lane l
+// writes LDS address lds + 16 l).  Written as inline asm so that the compiler's wait-count
+// bookkeeping does not see an LDS-DMA write: it would otherwise make LDS reads that it
+// cannot prove disjoint wait for every outstanding tile request (vmcnt(0)).  Tile requests
+// are waited for explicitly and ordered against their readers by the workgroup barrier.
+__device__ __forceinline__ void dma_chunk(const uint8_t* base, uint32_t lane_off, const uint8_t* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const lds_void_t*)lds;  // LDS byte address
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(base), "s"(m0)
+               : "memory", "m0");
+}
+
 struct Pipe {
   v16f oacc[4];  // O^T, 32 channels x 32 queries per tile
   v4i qop[4];            // this wave's Q operand (register copy)
   const uint8_t* qlds;   // this wave's Q operand in LDS
-  v8i pb[2];     // E4M3 probabilities of epochs of even / odd stage (PV deferred one step)
+  v8i pb[2];     // E4M3 probabilities of even / odd epochs (PV deferred one step)
   float alpha_prev;  // its rescale factor, applied to O just before its PV is accumulated
   float m, dpart, sig_q;
   const_f32* ksc;   // K block scales, read through the scalar cache
@@ -141,18 +159,15 @@ struct Dump {
   bool on;
 };
 
-// Each epoch moves 1024 16-byte chunks (K tile, then V tile) into stage ST; wave w, step
-// j covers chunks j*512 + w*64 + lane, which lie in one tile (wave-uniform LDS base).
-template <int ST>
-__device__ __forceinline__ void issue_tile(const Pipe& c, int e) {
+// A tile (8 KiB = 512 16-byte chunks) moves into an LDS slot; loader wave w, step j covers
+// chunks (j * kLoaderWaves + w) * 64 + lane (a wave-uniform LDS base per instruction).
+__device__ __forceinline__ void issue_tile(const Pipe& c, const uint8_t* src_tiles, int e, uint8_t* slot) {
   if (c.wave >= kLoaderWaves) return;
+  const uint8_t* tile = src_tiles + (int64_t)e * kTileBytes;  // wave-uniform
 #pragma unroll
-  for (int j = 0; j < kLoadsPerThread; ++j) {
-    const int c0 = j * kLoaderWaves * 64 + c.wave * 64;  // wave-uniform
-    const int which = c0 >> 9, cw = c0 & 511;
-    const uint8_t* base = (which ? c.vg : c.kg) + (int64_t)e * kTileBytes + cw * 16;  // uniform
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(base + c.lane * 16),
-                                     (lds_void_t*)(stage<ST>() + which * kTileBytes + cw * 16), 16, 0, 0);
+  for (int j = 0; j < kChunksPerTile; ++j) {
+    const int c0 = (j * kLoaderWaves + c.wave) * 64;
+    dma_chunk(tile + c0 * 16, (uint32_t)c.lane << 4, slot + c0 * 16);
   }
 }
 
@@ -206,7 +221,7 @@ __device__ __forceinline__ float softmax_pv(Pipe& c, v16i (&acc)[2], float sig, 
       const int key = 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
       v[j] = (TAIL && key >= kvalid) ? INT_MIN : acc[t][r];
     }
-    mx4[q] = max(max(max(v[0], v[1]), max(v[2], v[3])), max(max(v[4], v[5]), max(v[6], v[7])));
+    mx4[q] = max(max(max(max(v[0], v[1]), v[2]), max(max(v[3], v[4]), v[5])), max(v[6], v[7]));
   }
   int mx = max(max(mx4[0], mx4[1]), max(mx4[2], mx4[3]));
   mx = xhalf_max(mx);
@@ -275,19 +290,25 @@ __device__ __forceinline__ void rescale(Pipe& c) {
   }
 }
 
-// Pipeline step for epoch e held in stage ST.  Its scores are already in acc (QK issued
-// during the previous step).  Wait for tile e+1, start tile e+2, then (active waves)
+// Pipeline step for epoch e (ST = e % kUnroll).  Its scores are already in acc (QK issued
+// during the previous step).  Wait until K(e+1) and V(e-1) have landed (the requests of
+// step e-1 may stay in flight), barrier, request K(e+3) and V(e+1), then (active waves)
 // rescale O by alpha(e-1) and run the softmax of e with PV(e-1) and QK(e+1) interleaved.
 // LAST marks the final epoch (TAIL masks its keys), which also accumulates its own PV.
 template <int ST, bool LAST, bool TAIL, bool DUMP>
 __device__ __forceinline__ void pipe_step(Pipe& c, int e, int kvalid, const Dump& dump, v16i (&acc)[2]) {
-  constexpr int ST_PREV = (ST + kStages - 1) % kStages, ST_NEXT = (ST + 1) % kStages,
-                ST_PF = (ST + kPrefetch) % kStages;
-  // Tile e+1 must have landed; tiles e+2 .. e+kPrefetch-1 may still be in flight.
-  if (e + kPrefetch - 1 < c.nkb) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kPrefetch - 2) * kLoadsPerThread) : "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();  // tile e+1 visible to every wave; every wave is done with step e-1
-  if (e + kPrefetch < c.nkb) issue_tile<ST_PF>(c, e + kPrefetch);
+  constexpr int KS = ST % kRing, KN = (ST + 1) % kRing, VP = (ST + 2) % kRing;
+  if constexpr (LAST || DUMP) {
+    // LAST: V(e) too, its PV runs in this step.  DUMP: the score dump's stores (and any
+    // scratch traffic) share the counter, so the counts below would not hold.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (e + 2 < c.nkb) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kChunksPerTile) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kChunksPerTile) : "memory");
+  }
+  barrier();  // K(e+1), V(e-1) visible to every wave; every wave is done with step e-1
+  if (e + 3 < c.nkb) issue_tile(c, c.kg, e + 3, kslot<KS>());  // slot of K(e), read in step e-1
+  if (e + 1 < c.nkb) issue_tile(c, c.vg, e + 1, vslot<KN>());  // slot of V(e-2), read in step e-1
   if (!c.active) return;
   rescale(c);  // O = RO(e-2) * alpha(e-1), so PV(e-1) below completes RO(e-1)
   const float sig = c.sig_q * c.ks_next;  // fl32(fl32(q_scale * c) * k_scale)
@@ -307,12 +328,12 @@ __device__ __forceinline__ void pipe_step(Pipe& c, int e, int kvalid, const Dump
         }
     }
   }
-  c.alpha_prev = softmax_pv<TAIL, !LAST>(c, acc, sig, kvalid, c.pb[ST & 1], c.pb[(ST + 1) & 1],
-                                         stage<ST_PREV>() + kTileBytes, stage<ST_NEXT>());
+  c.alpha_prev = softmax_pv<TAIL, !LAST>(c, acc, sig, kvalid, c.pb[ST & 1], c.pb[(ST + 1) & 1], vslot<VP>(),
+                                         kslot<KN>());
   if constexpr (LAST) {
     rescale(c);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) pv_tile(c.oacc[w], stage<ST>() + kTileBytes, c.pb[ST & 1], c.lane, w);
+    for (int w = 0; w < 4; ++w) pv_tile(c.oacc[w], vslot<KS>(), c.pb[ST & 1], c.lane, w);
   }
 }
 
@@ -322,23 +343,23 @@ __device__ __forceinline__ void last_step(Pipe& c, int e, int kvalid, const Dump
   else pipe_step<ST, true, true, DUMP>(c, e, kvalid, dump, acc);
 }
 
-// kStages full steps e .. e+kStages-1 (stages 0 .. kStages-1).
+// kUnroll full steps e .. e+kUnroll-1 (e a multiple of kUnroll).
 template <bool DUMP, int... STs>
 __device__ __forceinline__ void steps_all(Pipe& c, int e, const Dump& dump, v16i (&acc)[2],
                                           std::integer_sequence<int, STs...>) {
   (pipe_step<STs, false, false, DUMP>(c, e + STs, kBlk, dump, acc), ...);
 }
-// The remaining full steps e + ST < nfull (e a multiple of kStages).
+// The remaining full steps e + ST < nfull (e a multiple of kUnroll).
 template <bool DUMP, int... STs>
 __device__ __forceinline__ void steps_rest(Pipe& c, int e, int nfull, const Dump& dump, v16i (&acc)[2],
                                            std::integer_sequence<int, STs...>) {
   ((e + STs < nfull ? pipe_step<STs, false, false, DUMP>(c, e + STs, kBlk, dump, acc) : void()), ...);
 }
-// The last epoch nfull, in stage nfull % kStages.
+// The last epoch nfull (ST = nfull % kUnroll).
 template <bool DUMP, int... STs>
 __device__ __forceinline__ void step_last(Pipe& c, int nfull, int kvalid, const Dump& dump, v16i (&acc)[2],
                                           std::integer_sequence<int, STs...>) {
-  const int st = nfull % kStages;
+  const int st = nfull % kUnroll;
   ((st == STs ? last_step<STs, DUMP>(c, nfull, kvalid, dump, acc) : void()), ...);
 }
 
@@ -413,6 +434,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
       else
         c.qop[u] = *reinterpret_cast<const v4i*>(src);
     }
+    // Retire the Q loads here, with a wait the compiler sees: otherwise its wait-count
+    // bookkeeping keeps them pending into the epoch loop and waits on vmcnt before the QK
+    // MFMAs there, which would also wait for the tile requests in flight.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     c.sig_q = p.q_scale[(int64_t)h * p.qblk_cap + qi.blk0 + qb] * p.c32;  // fl32(q_scale * c)
   }
   const int64_t ktile0 = (int64_t)h * p.kblk_cap + ki.blk0;
@@ -430,30 +455,27 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   dump.on = DUMP && s == p.dump_seg && h == p.dump_head;
 
   // ---------------------------------------------------------------- epoch pipeline
-  // Epoch e lives in stage e % kStages.  Step e reads the V tile of epoch e-1 and the K
-  // tile of epoch e+1 while tile e+kPrefetch streams in.  The V half of the last stage
-  // starts as zeros: step 0's deferred PV multiplies it by all-zero probabilities.
+  // Step e reads K(e+1) and V(e-1).  Step 0's deferred PV multiplies the V slot of epoch
+  // -1 (slot 2, zeroed here) by all-zero probabilities.
 #pragma unroll
-  for (int i = tid; i < kTileBytes / 16; i += kWaves * 64)
-    reinterpret_cast<v4i*>(stage<kStages - 1>() + kTileBytes)[i] = v4i{0, 0, 0, 0};
+  for (int i = tid; i < kTileBytes / 16; i += kWaves * 64) reinterpret_cast<v4i*>(g_v2)[i] = v4i{0, 0, 0, 0};
   v16i acc[2];
-  // prologue: tiles 0 .. kPrefetch-1 into stages 0 .. kPrefetch-1 (never the zeroed one)
-  [&]<int... STs>(std::integer_sequence<int, STs...>) {
-    ((STs < nkb ? issue_tile<STs>(c, STs) : void()), ...);
-  }(std::make_integer_sequence<int, kPrefetch>{});
-  if (kPrefetch - 1 < nkb) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kPrefetch - 1) * kLoadsPerThread) : "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();  // Q, tile 0 and the zeroed stage visible
+  if (nkb > 0) issue_tile(c, c.kg, 0, kslot<0>());
+  if (nkb > 1) issue_tile(c, c.kg, 1, kslot<1>());
+  if (nkb > 2) issue_tile(c, c.kg, 2, kslot<2>());
+  if (nkb > 0) issue_tile(c, c.vg, 0, vslot<0>());
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  barrier();  // Q, K(0) and the zeroed V slot visible
   if (c.active && nkb > 0) {
-    qk_tile(acc[0], stage<0>(), c.qop, c.qlds, lane, 0);
-    qk_tile(acc[1], stage<0>(), c.qop, c.qlds, lane, 1);
+    qk_tile(acc[0], kslot<0>(), c.qop, c.qlds, lane, 0);
+    qk_tile(acc[1], kslot<0>(), c.qop, c.qlds, lane, 1);
   }
   const int nfull = nkb - 1;  // epochs before the last one
   int e = 0;
-  for (; e + kStages <= nfull; e += kStages)
-    steps_all<DUMP>(c, e, dump, acc, std::make_integer_sequence<int, kStages>{});
-  steps_rest<DUMP>(c, e, nfull, dump, acc, std::make_integer_sequence<int, kStages - 1>{});
-  if (nkb > 0) step_last<DUMP>(c, nfull, last_valid, dump, acc, std::make_integer_sequence<int, kStages>{});
+  for (; e + kUnroll <= nfull; e += kUnroll)
+    steps_all<DUMP>(c, e, dump, acc, std::make_integer_sequence<int, kUnroll>{});
+  steps_rest<DUMP>(c, e, nfull, dump, acc, std::make_integer_sequence<int, kUnroll - 1>{});
+  if (nkb > 0) step_last<DUMP>(c, nfull, last_valid, dump, acc, std::make_integer_sequence<int, kUnroll>{});
 
   // ---------------------------------------------------------------- epilogue
   if (!c.active) return;
