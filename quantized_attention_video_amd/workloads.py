@@ -85,6 +85,11 @@ WORKLOADS = {
                                       "[L, 3, H, D] projection output"),
     "varlen_h24_4seg": Workload("varlen_h24_4seg", 5, H=24, seqlens=[37810, 8192, 1536, 100], layout="packed",
                                 notes="video, audio, short clip and text-only sequences, block-diagonal"),
+    # The roadmap's larger size (243 frames at 1344x768, "74K tokens") with the head count
+    # that its 7168-wide attention output implies at D=128 (56 heads).
+    "h3_video_l74000_h56": Workload("h3_video_l74000_h56", 6, H=56, B=1, Lq=74000, Lk=74000, k_bias_std=2.0,
+                                    layout="fused_qkv",
+                                    notes="~74K packed tokens, 56 heads; fused [L, 3, H, D] projection output"),
 }
 
 

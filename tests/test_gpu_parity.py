@@ -227,3 +227,46 @@ def test_queries_without_keys_give_zeros():
     ref = O.attention(oq, 0.1)
     _check_output(out[5:10].astype(np.float64), ref[5:10], "seg 1")
     assert np.all(ref[0:5] == 0) and np.all(ref[10:] == 0)
+
+
+@pytest.mark.timeout(900)
+def test_large_shape_sampled_heads():
+    """The 74K-token, 56-head shape in the bench's launch configuration: every quantized byte
+    and scale of three heads bit-exact, and sampled output rows of those heads in
+    tolerance.  The oracle runs on the three heads only (quantization and attention are
+    per head), the GPU on all 56."""
+    _need_gpu()
+    w = W.get("h3_video_l74000_h56")
+    _say(f"[case] {w.name}: generate + GPU")
+    inp = W.make_inputs(w)
+    quant, out = gpu_run(inp, w.sm_scale)
+    heads = [0, 29, 55]
+    _say(f"[case] {w.name}: oracle on heads {heads}")
+    sub = {n: W.packed_float64(inp[n][:, :, heads]) for n in "qkv"}
+    oq = O.quantize(sub["q"], sub["k"], sub["v"], inp["cu_q"], inp["cu_k"])
+    seg = oq[0]
+    nblk = -(-w.Lq // 64)
+    qt = quant.q.view(w.H, -1, 8192)
+    kt = quant.k.view(w.H, -1, 8192)
+    vt = quant.v.view(w.H, -1, 8192)
+    qs = quant.q_scale.view(w.H, -1)
+    ks = quant.k_scale.view(w.H, -1)
+    km = quant.k_mean.cpu().numpy()[0]
+    vsc = quant.v_scale.cpu().numpy()[0]
+    assert np.array_equal(km[heads], seg["k_mean"].astype(np.float32)), "k_mean"
+    assert np.array_equal(vsc[heads], seg["v_scale"].astype(np.float32)), "v_scale"
+    for j, h in enumerate(heads):
+        got_q = B.untile_qk(qt[h, :nblk].cpu().numpy())[:w.Lq]
+        got_k = B.untile_qk(kt[h, :nblk].cpu().numpy())[:w.Lk]
+        got_v = B.untile_v(vt[h, :nblk].cpu().numpy())[:w.Lk]
+        assert np.array_equal(got_q, seg["q8"][:, j, :].astype(np.int8)), f"q8 head {h}"
+        assert np.array_equal(got_k, seg["k8"][:, j, :].astype(np.int8)), f"k8 head {h}"
+        assert np.array_equal(got_v, seg["v8"][:, j, :].astype(np.uint8)), f"v8 head {h}"
+        assert np.array_equal(qs[h, :nblk].cpu().numpy(), seg["q_scale"][j].astype(np.float32)), f"q_scale {h}"
+        assert np.array_equal(ks[h, :nblk].cpu().numpy(), seg["k_scale"][j].astype(np.float32)), f"k_scale {h}"
+    rows = _sample_rows(w.Lq)
+    ref = O.attention(oq, w.sm_scale, rows={0: rows})[0]
+    got = out[0][rows][:, heads].float().cpu().numpy().astype(np.float64)
+    _check_output(got, ref, w.name)
+    assert torch.isfinite(out.float()).all()
+
