@@ -158,6 +158,7 @@ static sattn_status fwd_dense(const sattn_qkv_quant* qkv, int B, int H, int Lq, 
   p.o_st = o.stride_t; p.o_sh = o.stride_h;
   p.dump_acc = acc_out; p.dump_s = s_out;
   p.dump_seg = dump_seg; p.dump_head = dump_head; p.dump_lk = Lk;
+  p.max_kblocks = ceil64(Lk);
   const int qpw = attn_queries_per_wg();
   const int64_t ntile = ceil64(Lq) * 64 / qpw + (ceil64(Lq) * 64 % qpw != 0);
   const int64_t grid = 8 * (int64_t)((H + 7) / 8) * B * ntile;
@@ -205,6 +206,7 @@ sattn_status sattn_fwd_varlen(const sattn_qkv_quant* qkv, const int32_t* cu_seql
   p.o = static_cast<uint16_t*>(o.ptr);
   p.o_st = o.stride_t; p.o_sh = o.stride_h;
   p.dump_seg = -1; p.dump_head = -1;
+  p.max_kblocks = ceil64(k_clip);
   const int64_t tiles_bound = q_clip / attn_queries_per_wg() + nseg + 1;
   const int64_t grid = 8 * (int64_t)((H + 7) / 8) * tiles_bound;
   if (grid > 0x7fffffff) return SATTN_EUNSUPPORTED;

@@ -99,6 +99,12 @@ __shared__ __attribute__((aligned(16))) uint8_t g_v0[kTileBytes];
 __shared__ __attribute__((aligned(16))) uint8_t g_v1[kTileBytes];
 __shared__ __attribute__((aligned(16))) uint8_t g_v2[kTileBytes];
 __shared__ __attribute__((aligned(16))) uint8_t g_qop[kQInLds ? kWaves : 1][kQInLds ? 4096 : 16];  // Q operands
+// K block scales of the workgroup's segment, copied to LDS at the start (segments of at
+// most kKsLds key blocks; longer ones read them through the scalar cache).  A scalar load
+// in flight would make every LDS wait of the step a full lgkmcnt(0) wait: SMEM results
+// return out of order on the counter that LDS reads share.
+constexpr int kKsLds = 2048;
+__shared__ float g_ks[kKsLds];
 constexpr int kChunksPerTile = kTileBytes / 16 / (kLoaderWaves * 64);  // per loader lane
 static_assert(kChunksPerTile * kLoaderWaves * 64 * 16 == kTileBytes, "tile split");
 
@@ -147,6 +153,7 @@ struct Pipe {
   const_f32* ksc;   // K block scales, read through the scalar cache
   float ks_next;    // scale of the next epoch, loaded one step ahead
   const uint8_t *kg, *vg;
+  uint32_t loff[kChunksPerTile];  // DMA lane offsets: this lane's 16 bytes of each chunk
   int lane, wave, g, nkb;
   bool active;
 };
@@ -165,10 +172,7 @@ __device__ __forceinline__ void issue_tile(const Pipe& c, const uint8_t* src_til
   if (c.wave >= kLoaderWaves) return;
   const uint8_t* tile = src_tiles + (int64_t)e * kTileBytes;  // wave-uniform
 #pragma unroll
-  for (int j = 0; j < kChunksPerTile; ++j) {
-    const int c0 = (j * kLoaderWaves + c.wave) * 64;
-    dma_chunk(tile + c0 * 16, (uint32_t)c.lane << 4, slot + c0 * 16);
-  }
+  for (int j = 0; j < kChunksPerTile; ++j) dma_chunk(tile, c.loff[j], slot + (j * kLoaderWaves + c.wave) * 1024);
 }
 
 // One S^T tile t: acc_t = K(keys 32t..32t+31) . Q^T over 128 channels, with the K operands
@@ -200,11 +204,11 @@ __device__ __forceinline__ void qk_tile(v16i& acc_t, const uint8_t* Kl, const v4
 // m and the lane's partial denominator (in units of 448*P), packs the E4M3 probabilities
 // into pb and returns alpha.  TAIL masks keys >= kvalid.
 //
-// The step is cut into four chunks of 8 probabilities (scheduling barriers between them).
-// Each chunk issues about 128 cycles of MFMA work whose LDS operands were read one chunk
-// earlier, so in-order issue never waits on LDS, then its VALU work: chunk 0 PV(e-1)
-// tiles 0,1; chunk 1 tiles 2,3 (the previous probabilities die half-way); chunk 2
-// QK(e+1) score tile 0 (consumed by chunks 0-1); score tile 1 follows chunk 3.
+// The step is cut into eight groups of four probabilities (scheduling barriers between
+// them).  Each group first issues one MFMA, so this wave never asks the matrix core for
+// two in a row: groups 0-3 the PV(e-1) tiles 0-3, groups 4-7 the four k-steps of QK(e+1)
+// score tile 0 (whose scores groups 0-3 consumed); score tile 1 follows group 7.  The LDS
+// operands of each MFMA are read one to two groups ahead of it.
 template <bool TAIL, bool NEXT>
 __device__ __forceinline__ float softmax_pv(Pipe& c, v16i (&acc)[2], float sig, int kvalid, v8i& pb,
                                             const v8i& pb_prev, const uint8_t* Vprev, const uint8_t* Knext) {
@@ -231,48 +235,48 @@ __device__ __forceinline__ float softmax_pv(Pipe& c, v16i (&acc)[2], float sig, 
   const float mm = m_new - kLog2_448;
   float ps[4] = {0.f, 0.f, 0.f, 0.f};
   v4i ka[4];
+  const v16i zero = {};
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int j = 0; j < 8; ++j) {
     __builtin_amdgcn_sched_barrier(0);
-    if (w < 2) {  // PV(e-1): operands read one chunk ago
-      pv_mfma(c.oacc[2 * w], va, pb_prev);
-      pv_mfma(c.oacc[2 * w + 1], vb, pb_prev);
-      if (w == 0) {
-        va = load_v(Vprev, c.lane, 2);
-        vb = load_v(Vprev, c.lane, 3);
+    if (j < 4) {
+      pv_mfma(c.oacc[j], (j & 1) ? vb : va, pb_prev);
+      if (j == 0) va = load_v(Vprev, c.lane, 2);
+      if (j == 1) vb = load_v(Vprev, c.lane, 3);
+      if constexpr (NEXT) {
+        if (j >= 2) {
+          ka[2 * (j - 2)] = load_k(Knext, c.lane, 0, 2 * (j - 2));
+          ka[2 * (j - 2) + 1] = load_k(Knext, c.lane, 0, 2 * (j - 2) + 1);
+        }
       }
+    } else if constexpr (NEXT) {
+      const int u = j - 4;
+      acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[u], c.qop[u], u == 0 ? zero : acc[0], 0, 0, 0);
+      ka[u] = load_k(Knext, c.lane, 1, u);
     }
-    if constexpr (NEXT) {
-      if (w == 2) qk_mfma(acc[0], ka, c.qop, c.qlds, c.lane);  // operands read in chunk 1
-      if (w == 1 || w == 2) {                                   // operands of score tile w-1
+    const int t = j >> 2, q4 = j & 3;
+    float pv[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) ka[u] = load_k(Knext, c.lane, w - 1, u);
-      }
+    for (int r3 = 0; r3 < 4; ++r3) {
+      float arg = __builtin_fmaf((float)acc[t][4 * q4 + r3], sig, -mm);
+      if (TAIL && 32 * t + 8 * q4 + 4 * g + r3 >= kvalid) arg = -INFINITY;
+      pv[r3] = __builtin_amdgcn_exp2f(arg);  // 448 * P
+      ps[r3] += pv[r3];
     }
-    __builtin_amdgcn_sched_barrier(0);  // MFMA issue and operand reads ahead of the VALU
-    const int t = w >> 1;
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int q4 = 2 * (w & 1) + h2;
-      float pv[4];
-#pragma unroll
-      for (int r3 = 0; r3 < 4; ++r3) {
-        float arg = __builtin_fmaf((float)acc[t][4 * q4 + r3], sig, -mm);
-        if (TAIL && 32 * t + 8 * q4 + 4 * g + r3 >= kvalid) arg = -INFINITY;
-        pv[r3] = __builtin_amdgcn_exp2f(arg);  // 448 * P
-        ps[r3] += pv[r3];
-      }
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Wuninitialized"
-      int old;  // both halves of the word are written below; no register needs zeroing
-      int w01 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], old, false);
+    int old;  // both halves of the word are written below; no register needs zeroing
+    int w01 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], old, false);
 #pragma clang diagnostic pop
-      w01 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w01, true);
-      pb[4 * t + q4] = w01;
-    }
+    w01 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w01, true);
+    pb[j] = w01;
   }
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (NEXT) qk_mfma(acc[1], ka, c.qop, c.qlds, c.lane);
+  if constexpr (NEXT) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[u], c.qop[u], u == 0 ? zero : acc[1], 0, 0, 0);
+  }
   c.dpart = c.dpart * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
   c.m = m_new;
   return alpha;
@@ -290,12 +294,13 @@ __device__ __forceinline__ void rescale(Pipe& c) {
   }
 }
 
-// Pipeline step for epoch e (ST = e % kUnroll).  Its scores are already in acc (QK issued
+// Pipeline step for epoch e (ST = e % kUnroll).  STEADY steps have e + 3 < nkb: every
+// tile request and scale load is in range, so they run without tests or branches.  Its scores are already in acc (QK issued
 // during the previous step).  Wait until K(e+1) and V(e-1) have landed (the requests of
-// step e-1 may stay in flight), barrier, request K(e+3) and V(e+1), then (active waves)
+// step e-1 may stay in flight), barrier, request K(e+3) and V(e+1), then
 // rescale O by alpha(e-1) and run the softmax of e with PV(e-1) and QK(e+1) interleaved.
 // LAST marks the final epoch (TAIL masks its keys), which also accumulates its own PV.
-template <int ST, bool LAST, bool TAIL, bool DUMP>
+template <int ST, bool LAST, bool TAIL, bool DUMP, bool KSL, bool STEADY = false>
 __device__ __forceinline__ void pipe_step(Pipe& c, int e, int kvalid, const Dump& dump, v16i (&acc)[2]) {
   constexpr int KS = ST % kRing, KN = (ST + 1) % kRing, VP = (ST + 2) % kRing;
   if constexpr (LAST || DUMP) {
@@ -303,16 +308,16 @@ __device__ __forceinline__ void pipe_step(Pipe& c, int e, int kvalid, const Dump
     // scratch traffic) share the counter, so the counts below would not hold.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else {
-    if (e + 2 < c.nkb) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kChunksPerTile) : "memory");
+    if (STEADY || e + 2 < c.nkb) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kChunksPerTile) : "memory");
     else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kChunksPerTile) : "memory");
   }
   barrier();  // K(e+1), V(e-1) visible to every wave; every wave is done with step e-1
-  if (e + 3 < c.nkb) issue_tile(c, c.kg, e + 3, kslot<KS>());  // slot of K(e), read in step e-1
-  if (e + 1 < c.nkb) issue_tile(c, c.vg, e + 1, vslot<KN>());  // slot of V(e-2), read in step e-1
+  if (STEADY || e + 3 < c.nkb) issue_tile(c, c.kg, e + 3, kslot<KS>());  // slot of K(e), read in step e-1
+  if (STEADY || e + 1 < c.nkb) issue_tile(c, c.vg, e + 1, vslot<KN>());  // slot of V(e-2), read in step e-1
   if (!c.active) return;
   rescale(c);  // O = RO(e-2) * alpha(e-1), so PV(e-1) below completes RO(e-1)
   const float sig = c.sig_q * c.ks_next;  // fl32(fl32(q_scale * c) * k_scale)
-  if (e + 1 < c.nkb) c.ks_next = c.ksc[e + 1];
+  if (STEADY || e + 1 < c.nkb) c.ks_next = KSL ? g_ks[e + 1] : c.ksc[e + 1];
   if constexpr (DUMP) {
     if (dump.on && dump.row < dump.len_q) {
 #pragma unroll
@@ -337,33 +342,33 @@ __device__ __forceinline__ void pipe_step(Pipe& c, int e, int kvalid, const Dump
   }
 }
 
-template <int ST, bool DUMP>
+template <int ST, bool DUMP, bool KSL>
 __device__ __forceinline__ void last_step(Pipe& c, int e, int kvalid, const Dump& dump, v16i (&acc)[2]) {
-  if (kvalid == kBlk) pipe_step<ST, true, false, DUMP>(c, e, kBlk, dump, acc);
-  else pipe_step<ST, true, true, DUMP>(c, e, kvalid, dump, acc);
+  if (kvalid == kBlk) pipe_step<ST, true, false, DUMP, KSL>(c, e, kBlk, dump, acc);
+  else pipe_step<ST, true, true, DUMP, KSL>(c, e, kvalid, dump, acc);
 }
 
 // kUnroll full steps e .. e+kUnroll-1 (e a multiple of kUnroll).
-template <bool DUMP, int... STs>
+template <bool DUMP, bool KSL, bool STEADY, int... STs>
 __device__ __forceinline__ void steps_all(Pipe& c, int e, const Dump& dump, v16i (&acc)[2],
                                           std::integer_sequence<int, STs...>) {
-  (pipe_step<STs, false, false, DUMP>(c, e + STs, kBlk, dump, acc), ...);
+  (pipe_step<STs, false, false, DUMP, KSL, STEADY>(c, e + STs, kBlk, dump, acc), ...);
 }
 // The remaining full steps e + ST < nfull (e a multiple of kUnroll).
-template <bool DUMP, int... STs>
+template <bool DUMP, bool KSL, int... STs>
 __device__ __forceinline__ void steps_rest(Pipe& c, int e, int nfull, const Dump& dump, v16i (&acc)[2],
                                            std::integer_sequence<int, STs...>) {
-  ((e + STs < nfull ? pipe_step<STs, false, false, DUMP>(c, e + STs, kBlk, dump, acc) : void()), ...);
+  ((e + STs < nfull ? pipe_step<STs, false, false, DUMP, KSL>(c, e + STs, kBlk, dump, acc) : void()), ...);
 }
 // The last epoch nfull (ST = nfull % kUnroll).
-template <bool DUMP, int... STs>
+template <bool DUMP, bool KSL, int... STs>
 __device__ __forceinline__ void step_last(Pipe& c, int nfull, int kvalid, const Dump& dump, v16i (&acc)[2],
                                           std::integer_sequence<int, STs...>) {
   const int st = nfull % kUnroll;
-  ((st == STs ? last_step<STs, DUMP>(c, nfull, kvalid, dump, acc) : void()), ...);
+  ((st == STs ? last_step<STs, DUMP, KSL>(c, nfull, kvalid, dump, acc) : void()), ...);
 }
 
-template <bool DUMP>
+template <bool DUMP, bool KSL>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd, kWavesPerSimd))) void attn_fwd_kernel(AttnParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level addressing in SGPRs
@@ -411,6 +416,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   c.g = lane >> 5;
   c.nkb = nkb;
   c.active = qb < ceil_blocks(qi.len);
+#pragma unroll
+  for (int j = 0; j < kChunksPerTile; ++j) c.loff[j] = (uint32_t)(((j * kLoaderWaves + wave) * 64 + lane) * 16);
   c.m = -INFINITY;
   c.dpart = 0.f;
   c.sig_q = 0.f;
@@ -444,7 +451,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   c.kg = reinterpret_cast<const uint8_t*>(p.k8) + ktile0 * kTileBytes;
   c.vg = p.v8 + ktile0 * kTileBytes;
   c.ksc = (const_f32*)(p.k_scale + ktile0);
-  c.ks_next = nkb > 0 ? c.ksc[0] : 0.f;
+  if constexpr (KSL) {  // landed by the barrier before the first step
+    for (int i = tid; i < nkb; i += kWaves * 64) g_ks[i] = c.ksc[i];
+  } else {
+    c.ks_next = nkb > 0 ? c.ksc[0] : 0.f;
+  }
 
   Dump dump;
   dump.acc = p.dump_acc;
@@ -465,17 +476,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   if (nkb > 2) issue_tile(c, c.kg, 2, kslot<2>());
   if (nkb > 0) issue_tile(c, c.vg, 0, vslot<0>());
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  barrier();  // Q, K(0) and the zeroed V slot visible
-  if (c.active && nkb > 0) {
+  barrier();  // Q, K(0), the K scales and the zeroed V slot visible
+  if constexpr (KSL) c.ks_next = nkb > 0 ? g_ks[0] : 0.f;
+  if (nkb > 0) {
     qk_tile(acc[0], kslot<0>(), c.qop, c.qlds, lane, 0);
     qk_tile(acc[1], kslot<0>(), c.qop, c.qlds, lane, 1);
   }
   const int nfull = nkb - 1;  // epochs before the last one
   int e = 0;
-  for (; e + kUnroll <= nfull; e += kUnroll)
-    steps_all<DUMP>(c, e, dump, acc, std::make_integer_sequence<int, kUnroll>{});
-  steps_rest<DUMP>(c, e, nfull, dump, acc, std::make_integer_sequence<int, kUnroll - 1>{});
-  if (nkb > 0) step_last<DUMP>(c, nfull, last_valid, dump, acc, std::make_integer_sequence<int, kUnroll>{});
+  for (; e + kUnroll + 2 < nkb; e += kUnroll)  // every request of these steps is in range
+    steps_all<DUMP, KSL, true>(c, e, dump, acc, std::make_integer_sequence<int, kUnroll>{});
+  if (e + kUnroll <= nfull) {
+    steps_all<DUMP, KSL, false>(c, e, dump, acc, std::make_integer_sequence<int, kUnroll>{});
+    e += kUnroll;
+  }
+  steps_rest<DUMP, KSL>(c, e, nfull, dump, acc, std::make_integer_sequence<int, kUnroll - 1>{});
+  if (nkb > 0) step_last<DUMP, KSL>(c, nfull, last_valid, dump, acc, std::make_integer_sequence<int, kUnroll>{});
 
   // ---------------------------------------------------------------- epilogue
   if (!c.active) return;
@@ -562,10 +578,13 @@ hipError_t launch_plan(const int32_t* cu_q, const int32_t* cu_k, int nseg, int64
 
 hipError_t launch_attention(const AttnParams& p, int64_t grid, bool dump, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  if (dump)
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, p);
+  const bool ksl = p.max_kblocks <= kKsLds;
+  if (dump)  // the score dump is a debugging path: scales through the scalar cache
+    hipLaunchKernelGGL((attn_fwd_kernel<true, false>), dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, p);
+  else if (ksl)
+    hipLaunchKernelGGL((attn_fwd_kernel<false, true>), dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<false, false>), dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -47,6 +47,7 @@ struct AttnParams {
   float* dump_s;
   int dump_seg, dump_head;
   int64_t dump_lk;
+  int64_t max_kblocks;  // bound on any segment's key blocks (selects the K-scale path)
 };
 
 int stats_chunks(int nseg, int H);
