@@ -18,11 +18,12 @@
 //    owns one query column and 32 of the epoch's 64 keys, so the row max and row sum are
 //    in-lane plus one v_permlane32_swap between the two half-waves.
 //  * The row max is taken on the INT32 accumulators (sigma > 0, and rounding is
-//    monotone, so max_j fl32(acc_j*sigma) = fl32(max_j acc_j * sigma) exactly).  Each
-//    accumulator is converted exactly to FP32 and one FMA, acc*sigma - (m' - log2 448),
-//    gives the base-2 exponent of 448*P with a single rounding.  (Folding a large
-//    constant into that FMA to skip the conversion perturbs P by ~1e-4..1e-3 per epoch,
-//    enough to flip E4M3 roundings of the dominant keys in peaked rows.)
+//    monotone, so max_j fl32(acc_j*sigma) = fl32(max_j acc_j * sigma) exactly).  The
+//    accumulators start at the bit pattern of 1.5 * 2^23, so each one read as FP32 minus
+//    1.5 * 2^23 is the exact accumulator value (one subtraction, no conversion), and one
+//    FMA, acc*sigma - (m' - log2 448), gives the base-2 exponent of 448*P with a single
+//    rounding.  (Folding the 1.5 * 2^23 * sigma term into that FMA instead perturbs P by
+//    ~1e-4..1e-3, enough to flip E4M3 roundings of the dominant keys in peaked rows.)
 //  * The lane's 32 probabilities are packed with v_cvt_pk_fp8_f32 directly into the B
 //    operand of v_mfma_f32_32x32x64_f8f6f4 (O^T += V^T P^T).  The V tile is stored by the
 //    quantizer with its keys permuted to match, so no probability goes through LDS.
@@ -56,6 +57,12 @@ constexpr int kWavesPerSimd = kWaves > 4 ? kWaves / 4 : 2;
 constexpr int kQPerWG = kWaves * 32;       // queries per workgroup
 constexpr int kQBlocksPerWG = kWaves / 2;  // 64-query blocks per workgroup
 constexpr float kLog2_448 = 8.8073549220576041f;
+// The QK accumulators start at kAccBias instead of 0: read as FP32, kAccBias + acc is
+// exactly 12582912 + acc for |acc| < 2^22 (INT8 products over 128 channels stay below
+// 127^2 * 128 < 2^21), so one exact subtraction replaces the integer conversion, and the
+// biased words still order like the accumulators for the integer row max.
+constexpr int kAccBias = 0x4B400000;
+constexpr float kAccBiasF = 12582912.0f;
 
 int attn_queries_per_wg() { return kQPerWG; }
 
@@ -146,6 +153,7 @@ __device__ __forceinline__ void dma_chunk(const uint8_t* base, uint32_t lane_off
 struct Pipe {
   v16f oacc[4];  // O^T, 32 channels x 32 queries per tile
   v4i qop[4];            // this wave's Q operand (register copy)
+  v16i bias;             // kAccBias in every element: the start value of the QK accumulators
   const uint8_t* qlds;   // this wave's Q operand in LDS
   v8i pb[2];     // E4M3 probabilities of even / odd epochs (PV deferred one step)
   float alpha_prev;  // its rescale factor, applied to O just before its PV is accumulated
@@ -181,7 +189,7 @@ __device__ __forceinline__ void issue_tile(const Pipe& c, const uint8_t* src_til
 __device__ __forceinline__ void qk_mfma(v16i& acc_t, const v4i (&ka)[4], const v4i (&qop)[4], const uint8_t* Ql,
                                         int lane) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc_t[i] = 0;
+  for (int i = 0; i < 16; ++i) acc_t[i] = kAccBias;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     v4i b;
@@ -215,27 +223,29 @@ __device__ __forceinline__ float softmax_pv(Pipe& c, v16i (&acc)[2], float sig, 
   const int g = c.g;
   v8i va = load_v(Vprev, c.lane, 0), vb = load_v(Vprev, c.lane, 1);
   __builtin_amdgcn_sched_barrier(0);  // the reads go out first; the row max hides them
-  int mx4[4];
+  int v[32];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {  // four independent max chains of 8 (t = q/2, rows 8(q%2)..)
-    int v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int t = q >> 1, r = 8 * (q & 1) + j;
-      const int key = 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-      v[j] = (TAIL && key >= kvalid) ? INT_MIN : acc[t][r];
-    }
-    mx4[q] = max(max(max(max(v[0], v[1]), v[2]), max(max(v[3], v[4]), v[5])), max(v[6], v[7]));
+  for (int i = 0; i < 32; ++i) {
+    const int t = i >> 4, r = i & 15;
+    const int key = 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
+    v[i] = (TAIL && key >= kvalid) ? INT_MIN : acc[t][r];
   }
-  int mx = max(max(mx4[0], mx4[1]), max(mx4[2], mx4[3]));
+  int m1[12];  // a three-input max tree: 10 + 4 + 1 v_max3 and one v_max
+#pragma unroll
+  for (int i = 0; i < 10; ++i) m1[i] = max(max(v[3 * i], v[3 * i + 1]), v[3 * i + 2]);
+  m1[10] = v[30];
+  m1[11] = v[31];
+  int m2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m2[i] = max(max(m1[3 * i], m1[3 * i + 1]), m1[3 * i + 2]);
+  int mx = max(max(max(m2[0], m2[1]), m2[2]), m2[3]);
   mx = xhalf_max(mx);
-  const float smax = (float)mx * sig;  // = max_j fl32(acc_j * sig)
+  const float smax = (float)(mx - kAccBias) * sig;  // = max_j fl32(acc_j * sig)
   const float m_new = fmaxf(c.m, smax);
   const float alpha = __builtin_amdgcn_exp2f(c.m - m_new);  // 0 on the first epoch
   const float mm = m_new - kLog2_448;
   float ps[4] = {0.f, 0.f, 0.f, 0.f};
   v4i ka[4];
-  const v16i zero = {};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     __builtin_amdgcn_sched_barrier(0);
@@ -251,14 +261,14 @@ __device__ __forceinline__ float softmax_pv(Pipe& c, v16i (&acc)[2], float sig, 
       }
     } else if constexpr (NEXT) {
       const int u = j - 4;
-      acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[u], c.qop[u], u == 0 ? zero : acc[0], 0, 0, 0);
+      acc[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[u], c.qop[u], u == 0 ? c.bias : acc[0], 0, 0, 0);
       ka[u] = load_k(Knext, c.lane, 1, u);
     }
     const int t = j >> 2, q4 = j & 3;
     float pv[4];
 #pragma unroll
     for (int r3 = 0; r3 < 4; ++r3) {
-      float arg = __builtin_fmaf((float)acc[t][4 * q4 + r3], sig, -mm);
+      float arg = __builtin_fmaf(__int_as_float(acc[t][4 * q4 + r3]) - kAccBiasF, sig, -mm);
       if (TAIL && 32 * t + 8 * q4 + 4 * g + r3 >= kvalid) arg = -INFINITY;
       pv[r3] = __builtin_amdgcn_exp2f(arg);  // 448 * P
       ps[r3] += pv[r3];
@@ -275,7 +285,7 @@ __device__ __forceinline__ float softmax_pv(Pipe& c, v16i (&acc)[2], float sig, 
   if constexpr (NEXT) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      acc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[u], c.qop[u], u == 0 ? zero : acc[1], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[u], c.qop[u], u == 0 ? c.bias : acc[1], 0, 0, 0);
   }
   c.dpart = c.dpart * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
   c.m = m_new;
@@ -327,8 +337,8 @@ __device__ __forceinline__ void pipe_step(Pipe& c, int e, int kvalid, const Dump
           const int key = 32 * t + 8 * (r >> 2) + 4 * c.g + (r & 3);
           if (key < kvalid) {
             const int64_t o = dump.row * dump.lk + (int64_t)e * kBlk + key;
-            dump.acc[o] = acc[t][r];
-            dump.s[o] = (float)acc[t][r] * sig;
+            dump.acc[o] = acc[t][r] - kAccBias;
+            dump.s[o] = (float)(acc[t][r] - kAccBias) * sig;
           }
         }
     }
@@ -422,6 +432,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   c.dpart = 0.f;
   c.sig_q = 0.f;
   c.alpha_prev = 1.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c.bias[i] = kAccBias;
+  asm volatile("" : "+v"(c.bias));  // kept in registers rather than rematerialised per use
 #pragma unroll
   for (int w = 0; w < 4; ++w)
 #pragma unroll
