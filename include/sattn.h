@@ -49,7 +49,9 @@
  *  q, k : int8,  [H][blk_cap][8192]: one 8 KiB tile per 64-token block in MFMA operand
  *         order.  Byte ((t*4 + u)*64 + g*32 + i)*16 + s of a tile holds token 32*t + i,
  *         channel 64*g + 16*u + s (t,g in {0,1}; u in 0..3; i in 0..31; s in 0..15).
- *  q_scale, k_scale : float, [H][blk_cap], the FP32 scale of each 64-token block.
+ *  q_scale : float, [H][qblk_cap][64 / q_scale_rows]: the FP32 scale of each 64-token
+ *         block, or of each 32-row half of it (q_scale_rows = 32).
+ *  k_scale : float, [H][kblk_cap], the FP32 scale of each 64-token block.
  *  k_mean : float, [nseg][H][128], the per-channel mean subtracted from K.
  *  v    : OCP E4M3 bytes, [H][kblk_cap][8192]: one tile per 64-key block, channel-major.
  *         Byte ((w*2 + f)*64 + g*32 + i)*16 + s holds channel 32*w + i and key
@@ -91,7 +93,12 @@ typedef struct {
   int64_t stride_b, stride_t, stride_h;
 } sattn_bf16_out;
 
-/* Caller-owned quantized Q/K/V buffers and their capacities (see the layout above). */
+/* Caller-owned quantized Q/K/V buffers and their capacities (see the layout above).
+ * q_scale_rows selects the Q scale granularity, read by sattn_quantize_qkv and by every
+ * forward entry point (the two must agree): 64 (or 0) = one scale per 64-token block,
+ * 32 = one scale per 32 query rows, the "per-warp INT8 Q" policy of the roadmap page's
+ * "Phase 4: Dense Sage-Compatible Attention" (a 128-query tile split over four QK warps);
+ * K keeps one scale per 64 tokens in both.  Any other value gives SATTN_EINVAL. */
 typedef struct {
   int8_t* q;
   float* q_scale;
@@ -101,12 +108,14 @@ typedef struct {
   uint8_t* v;
   float* v_scale;
   int64_t qblk_cap, kblk_cap;
+  int32_t q_scale_rows;
 } sattn_qkv_quant;
 
 /* Byte sizes of every buffer of sattn_qkv_quant, plus scratch sizes. */
 typedef struct {
   int64_t qblk_cap, kblk_cap;
   size_t q_bytes, q_scale_bytes, k_bytes, k_scale_bytes, k_mean_bytes, v_bytes, v_scale_bytes;
+                                /* q_scale_bytes holds either Q scale granularity     */
   size_t quant_workspace_bytes; /* workspace of sattn_quantize_qkv                     */
   size_t fwd_workspace_bytes;   /* workspace of sattn_fwd_varlen (0 is enough for dense) */
 } sattn_sizes;
@@ -135,7 +144,8 @@ SATTN_API sattn_status sattn_quant_query(int nseg, int64_t total_q, int64_t tota
  * For each segment s, head h, channel c (all sums in FP64, every scale operation a single
  * correctly rounded FP32 operation):
  *   k_mean[s,h,c] = fl32( (sum_t K[t,h,c]) / Lk_s ),  K' = fl32(K - k_mean)
- *   per 64-token block: amax = max|x|, scale = fl32(amax/127), inv = fl32(127/amax),
+ *   per 64-token block (Q: per 32 rows when out->q_scale_rows = 32): amax = max|x|,
+ *     scale = fl32(amax/127), inv = fl32(127/amax),
  *     code = clamp(rne(fl32(x*inv)), -127, 127)   (x = Q, or K'; amax = 0 → scale 0, codes 0)
  *   v_scale[s,h,c] = fl32(amax_V/448), V8 = e4m3_rne(fl32(V * fl32(448/amax_V)))
  *
@@ -153,7 +163,8 @@ SATTN_API sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, satt
  * "Attention forward" / prequantized mainloop, and the checkpoint list of the
  * Phase 2B report's "Exactness" section).  B segments of Lq queries and Lk keys, H heads,
  * D = 128.  sm_scale multiplies q·k (usually 1/sqrt(D)); it must be finite and > 0.
- * The score of query i and key j in 64-blocks (bq, bk) is
+ * The score of query i and key j in 64-blocks (bq, bk) is (bq: the 32-row block of i
+ * when qkv->q_scale_rows = 32)
  *   S = fl32(acc * sigma),  sigma = fl32(fl32(q_scale[bq] * c) * k_scale[bk]),
  *   c = fl32(sm_scale * log2(e)) computed in double on the host,
  * and the softmax runs in base 2.  o receives BF16 rows for every valid query token

@@ -12,7 +12,9 @@ Where the pages leave a step open, the plainest reading is taken:
   * the K mean is taken per (sequence, head, channel) over that sequence's keys, summed
     in FP64 and rounded once to FP32; the smoothed K is rounded once to FP32;
   * Q and smoothed K are quantized per 64-token block (symmetric, RNE, codes in
-    [-127, 127], scale = fl32(amax/127), multiply by fl32(127/amax));
+    [-127, 127], scale = fl32(amax/127), multiply by fl32(127/amax)); the "per-warp"
+    policy of the roadmap's Phase 4 is also available for Q as one scale per 32 query
+    rows (the rows one of four QK warps owns in a 128-query tile), K staying per 64;
   * V is quantized per (sequence, head, channel): scale fl32(amax/448), multiply by
     fl32(448/amax), E4M3 RNE;
   * sm_scale and log2(e) are folded into the per-block score scale
@@ -51,8 +53,8 @@ def sm_scale_log2(sm_scale):
     return float(fl32(float(np.float32(sm_scale)) * LOG2E))
 
 
-def quantize_int8_blocks(x):
-    """Symmetric INT8 quantization of [L, H, D] per 64-token block and head.
+def quantize_int8_blocks(x, block=None):
+    """Symmetric INT8 quantization of [L, H, D] per `block`-token block (default 64) and head.
 
     Returns codes [L, H, D] (float64 integers in [-127, 127]) and scales [H, nblk].
     scale = fl32(amax/127) and inv = fl32(127/amax) are each one correctly rounded
@@ -61,19 +63,20 @@ def quantize_int8_blocks(x):
     x*inv is exact in float64 (24 + 24 bits), so fl32 applies the single rounding.
     An all-zero block gets scale 0 and codes 0.
     """
+    block = BLOCK if block is None else block
     L, H, D = x.shape
-    nblk = -(-L // BLOCK)
+    nblk = -(-L // block)
     codes = np.zeros_like(x)
     scales = np.zeros((H, nblk))
     for b in range(nblk):
-        blk = x[b * BLOCK:(b + 1) * BLOCK]  # [n, H, D]; the last block may be partial
+        blk = x[b * block:(b + 1) * block]  # [n, H, D]; the last block may be partial
         amax = np.max(np.abs(blk), axis=(0, 2))  # [H]
         nz = amax > 0
         safe = np.where(nz, amax, 1.0)
         scale = np.where(nz, fl32(safe / 127.0), 0.0)
         inv = np.where(nz, fl32(127.0 / safe), 0.0)
         q = np.clip(rne(fl32(blk * inv[None, :, None])), -127.0, 127.0)
-        codes[b * BLOCK:(b + 1) * BLOCK] = q
+        codes[b * block:(b + 1) * block] = q
         scales[:, b] = scale
     return codes, scales
 
@@ -109,26 +112,29 @@ def quantize_v(v):
     return e4m3_encode(vals), vals, scale
 
 
-def quantize(q, k, v, cu_q, cu_k):
+def quantize(q, k, v, cu_q, cu_k, q_rows=None):
     """Quantize packed Q/K/V ([T, H, D] float64 holding BF16 values) per segment.
 
-    Returns a list with one dict per segment: q8 [Lq, H, D], q_scale [H, nqblk],
-    k_mean [H, D], k8 [Lk, H, D], k_scale [H, nkblk], v8 (uint8 codes) [Lk, H, D],
-    v8val [Lk, H, D], v_scale [H, D].
+    q_rows: query rows per Q scale, 64 (default, one per 64-token block) or 32 (the
+    per-warp variant).  Returns a list with one dict per segment: q8 [Lq, H, D], q_scale
+    [H, ceil(Lq/q_rows)], q_rows, k_mean [H, D], k8 [Lk, H, D], k_scale [H, nkblk], v8
+    (uint8 codes) [Lk, H, D], v8val [Lk, H, D], v_scale [H, D].
     """
+    q_rows = BLOCK if q_rows is None else q_rows
     out = []
     for (qs, qe), (ks, ke) in zip(segments(cu_q), segments(cu_k)):
-        q8, qsc = quantize_int8_blocks(q[qs:qe])
+        q8, qsc = quantize_int8_blocks(q[qs:qe], q_rows)
         km, kp = k_smooth(k[ks:ke])
         k8, ksc = quantize_int8_blocks(kp)
         v8, v8val, vsc = quantize_v(v[ks:ke])
-        out.append(dict(q8=q8, q_scale=qsc, k_mean=km, k8=k8, k_scale=ksc, v8=v8, v8val=v8val, v_scale=vsc))
+        out.append(dict(q8=q8, q_scale=qsc, q_rows=q_rows, k_mean=km, k8=k8, k_scale=ksc, v8=v8, v8val=v8val,
+                        v_scale=vsc))
     return out
 
 
 # ----------------------------------------------------------------------------- scores
 def block_sigma(q_scale_h, k_scale_h, c32):
-    """sigma[bq, bk] = fl32(fl32(q_scale[bq] * c) * k_scale[bk])."""
+    """sigma[bq, bk] = fl32(fl32(q_scale[bq] * c) * k_scale[bk]) (bq a block of q_rows queries)."""
     a = fl32(q_scale_h * c32)
     return fl32(a[:, None] * k_scale_h[None, :])
 
@@ -145,7 +151,7 @@ def scores(seg, h, sm_scale, rows=None):
     rows = np.arange(Lq) if rows is None else np.asarray(rows)
     acc = q8[rows] @ k8.T
     sig = block_sigma(seg["q_scale"][h], seg["k_scale"][h], sm_scale_log2(sm_scale))
-    sig_rows = sig[rows // BLOCK]  # [nrows, nkblk]
+    sig_rows = sig[rows // seg.get("q_rows", BLOCK)]  # [nrows, nkblk]
     sig_full = np.repeat(sig_rows, BLOCK, axis=1)[:, :Lk]
     return acc, fl32(acc * sig_full)
 
@@ -227,7 +233,7 @@ def softmax_attention_exact(q, k, v, sm_scale):
 def dequantized_inputs(seg):
     """The values the quantized program multiplies, per segment: Q8*sq, K8*sk, V8*sv."""
     L, H, D = seg["q8"].shape
-    qrep = np.repeat(seg["q_scale"], BLOCK, axis=1)[:, :L].T  # [L, H]
+    qrep = np.repeat(seg["q_scale"], seg.get("q_rows", BLOCK), axis=1)[:, :L].T  # [L, H]
     Lk = seg["k8"].shape[0]
     krep = np.repeat(seg["k_scale"], BLOCK, axis=1)[:, :Lk].T
     return (seg["q8"] * qrep[:, :, None], seg["k8"] * krep[:, :, None],

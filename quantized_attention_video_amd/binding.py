@@ -38,7 +38,8 @@ class BF16Out(ctypes.Structure):
 class QKVQuant(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("q_scale", ctypes.c_void_p), ("k", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("k_mean", ctypes.c_void_p), ("v", ctypes.c_void_p),
-                ("v_scale", ctypes.c_void_p), ("qblk_cap", ctypes.c_int64), ("kblk_cap", ctypes.c_int64)]
+                ("v_scale", ctypes.c_void_p), ("qblk_cap", ctypes.c_int64), ("kblk_cap", ctypes.c_int64),
+                ("q_scale_rows", ctypes.c_int32)]
 
 
 class Sizes(ctypes.Structure):
@@ -128,32 +129,37 @@ class Quantized:
     nseg: int
     H: int
     sizes: Sizes
+    q_scale_rows: int = 64  # query rows per Q scale: 64 or 32 (q_scale is [H, qblk_cap * 64 / rows])
 
     def struct(self):
         return QKVQuant(self.q.data_ptr(), self.q_scale.data_ptr(), self.k.data_ptr(), self.k_scale.data_ptr(),
                         self.k_mean.data_ptr(), self.v.data_ptr(), self.v_scale.data_ptr(), self.qblk_cap,
-                        self.kblk_cap)
+                        self.kblk_cap, self.q_scale_rows)
 
 
-def alloc_quantized(nseg, total_q, total_k, H, device="cuda"):
+def alloc_quantized(nseg, total_q, total_k, H, device="cuda", q_scale_rows=64):
     """Allocate (uninitialised) quantized buffers sized by sattn_quant_query."""
+    if q_scale_rows not in (32, 64):
+        raise ValueError("q_scale_rows must be 32 or 64")
     s = sattn_quant_query(nseg, total_q, total_k, H)
     e = dict(device=device)
     return Quantized(
         q=torch.empty((H, s.qblk_cap, 8192), dtype=torch.int8, **e),
-        q_scale=torch.empty((H, s.qblk_cap), dtype=torch.float32, **e),
+        q_scale=torch.empty((H, s.qblk_cap * (64 // q_scale_rows)), dtype=torch.float32, **e),
         k=torch.empty((H, s.kblk_cap, 8192), dtype=torch.int8, **e),
         k_scale=torch.empty((H, s.kblk_cap), dtype=torch.float32, **e),
         k_mean=torch.empty((nseg, H, D), dtype=torch.float32, **e),
         v=torch.empty((H, s.kblk_cap, 8192), dtype=torch.uint8, **e),
         v_scale=torch.empty((nseg, H, D), dtype=torch.float32, **e),
         workspace=torch.empty(max(s.quant_workspace_bytes, 16), dtype=torch.uint8, **e),
-        qblk_cap=s.qblk_cap, kblk_cap=s.kblk_cap, nseg=nseg, H=H, sizes=s)
+        qblk_cap=s.qblk_cap, kblk_cap=s.kblk_cap, nseg=nseg, H=H, sizes=s, q_scale_rows=q_scale_rows)
 
 
-def sattn_quantize_qkv(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, out=None, stream=None):
+def sattn_quantize_qkv(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, out=None, stream=None, q_scale_rows=64):
     """Quantize BF16 Q/K/V views.  Dense: [B, L, H, D] views.  Varlen: packed [T, H, D]
-    views plus device int32 cu_seqlens tensors of nseg+1 entries."""
+    views plus device int32 cu_seqlens tensors of nseg+1 entries.  q_scale_rows: 64 (one
+    Q scale per 64-token block) or 32 (one per 32 query rows); ignored when `out` is given
+    (its own q_scale_rows applies)."""
     varlen = cu_seqlens_q is not None
     if varlen:
         nseg = cu_seqlens_q.numel() - 1
@@ -165,7 +171,7 @@ def sattn_quantize_qkv(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, out=None, 
         Lk = k.shape[1]
         total_q, total_k = nseg * Lq, nseg * Lk
     if out is None:
-        out = alloc_quantized(nseg, total_q, total_k, H, device=q.device)
+        out = alloc_quantized(nseg, total_q, total_k, H, device=q.device, q_scale_rows=q_scale_rows)
     st = out.struct()
     _check(lib().sattn_quantize_qkv(_view(q, BF16In), _view(k, BF16In), _view(v, BF16In), nseg, H, D, Lq, Lk,
                                     _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), ctypes.byref(st),

@@ -41,8 +41,12 @@ size_t fwd_ws(int nseg) { return align_up((size_t)nseg * 4) + align_up(((size_t)
 
 bool quant_bufs_ok(const sattn_qkv_quant* b) {
   return b && b->q && b->q_scale && b->k && b->k_scale && b->k_mean && b->v && b->v_scale && aligned16(b->q) &&
-         aligned16(b->k) && aligned16(b->v) && b->qblk_cap >= 0 && b->kblk_cap >= 0;
+         aligned16(b->k) && aligned16(b->v) && b->qblk_cap >= 0 && b->kblk_cap >= 0 &&
+         (b->q_scale_rows == 0 || b->q_scale_rows == 32 || b->q_scale_rows == 64);
 }
+
+// log2(64 / q_scale_rows): Q scales per 64-token block, as a shift.
+int q_scale_shift(const sattn_qkv_quant* b) { return b->q_scale_rows == 32 ? 1 : 0; }
 
 int64_t ceil64(int64_t n) { return (n + 63) / 64; }
 
@@ -71,7 +75,7 @@ sattn_status sattn_quant_query(int nseg, int64_t total_q, int64_t total_k, int H
   out->qblk_cap = total_q / 64 + nseg;
   out->kblk_cap = total_k / 64 + nseg;
   out->q_bytes = (size_t)H * out->qblk_cap * kTileBytes;
-  out->q_scale_bytes = (size_t)H * out->qblk_cap * sizeof(float);
+  out->q_scale_bytes = (size_t)H * out->qblk_cap * 2 * sizeof(float);  // room for 32-row scales
   out->k_bytes = (size_t)H * out->kblk_cap * kTileBytes;
   out->k_scale_bytes = (size_t)H * out->kblk_cap * sizeof(float);
   out->k_mean_bytes = (size_t)nseg * H * kD * sizeof(float);
@@ -118,6 +122,7 @@ sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in 
   a.k8 = out->k; a.k_scale = out->k_scale; a.k_mean = out->k_mean;
   a.v8 = out->v; a.v_scale = out->v_scale;
   a.qblk_cap = out->qblk_cap; a.kblk_cap = out->kblk_cap;
+  a.q_scale_shift = q_scale_shift(out);
   a.workspace = workspace;
   a.ws_sums_bytes = ws.sums;
   a.ws_vmax_bytes = ws.vmax;
@@ -158,6 +163,7 @@ static sattn_status fwd_dense(const sattn_qkv_quant* qkv, int B, int H, int Lq, 
   p.o_st = o.stride_t; p.o_sh = o.stride_h;
   p.dump_acc = acc_out; p.dump_s = s_out;
   p.dump_seg = dump_seg; p.dump_head = dump_head; p.dump_lk = Lk;
+  p.q_scale_shift = q_scale_shift(qkv);
   p.max_kblocks = ceil64(Lk);
   const int qpw = attn_queries_per_wg();
   const int64_t ntile = ceil64(Lq) * 64 / qpw + (ceil64(Lq) * 64 % qpw != 0);
@@ -206,6 +212,7 @@ sattn_status sattn_fwd_varlen(const sattn_qkv_quant* qkv, const int32_t* cu_seql
   p.o = static_cast<uint16_t*>(o.ptr);
   p.o_st = o.stride_t; p.o_sh = o.stride_h;
   p.dump_seg = -1; p.dump_head = -1;
+  p.q_scale_shift = q_scale_shift(qkv);
   p.max_kblocks = ceil64(k_clip);
   const int64_t tiles_bound = q_clip / attn_queries_per_wg() + nseg + 1;
   const int64_t grid = 8 * (int64_t)((H + 7) / 8) * tiles_bound;

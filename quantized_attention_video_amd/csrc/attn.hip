@@ -458,7 +458,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     // bookkeeping keeps them pending into the epoch loop and waits on vmcnt before the QK
     // MFMAs there, which would also wait for the tile requests in flight.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    c.sig_q = p.q_scale[(int64_t)h * p.qblk_cap + qi.blk0 + qb] * p.c32;  // fl32(q_scale * c)
+    // fl32(q_scale * c) of this wave's 32 rows: the scale of their 64-row block, or of
+    // their own half of it with 32-row Q scales
+    const int64_t qsi = (((int64_t)h * p.qblk_cap + qi.blk0 + qb) << p.q_scale_shift) + (p.q_scale_shift ? hq : 0);
+    c.sig_q = p.q_scale[qsi] * p.c32;
   }
   const int64_t ktile0 = (int64_t)h * p.kblk_cap + ki.blk0;
   c.kg = reinterpret_cast<const uint8_t*>(p.k8) + ktile0 * kTileBytes;

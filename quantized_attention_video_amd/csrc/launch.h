@@ -23,6 +23,7 @@ struct QuantLaunch {
   uint8_t* v8;
   float* v_scale;
   int64_t qblk_cap, kblk_cap;
+  int q_scale_shift;  // Q scales per 64-token block: 1 << q_scale_shift
   void* workspace;
   size_t ws_sums_bytes, ws_vmax_bytes;
 };
@@ -48,6 +49,7 @@ struct AttnParams {
   int dump_seg, dump_head;
   int64_t dump_lk;
   int64_t max_kblocks;  // bound on any segment's key blocks (selects the K-scale path)
+  int q_scale_shift;    // Q scales per 64-token block: 1 << q_scale_shift (1 or 2)
 };
 
 int stats_chunks(int nseg, int H);

@@ -91,12 +91,14 @@ __global__ __launch_bounds__(kD) void finalize_kernel(SegGeom gk, int H, int nch
 
 // ---------------------------------------------------------------------------- Q / K
 // Grid (blocks, H), 256 threads.  Thread tid handles rows r = tid/16 + 16*i (i < 4) and
-// channels 8*(tid%16) .. +7 of the 64-token block: one 16-byte load per row.
+// channels 8*(tid%16) .. +7 of the 64-token block: one 16-byte load per row.  Rows 0..31
+// are i = 0, 1 and rows 32..63 are i = 2, 3, so with halves = 2 each 32-row half gets its
+// own amax and scale (scale_out then holds two scales per block).
 __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restrict__ x, SegGeom g, int64_t st,
                                                        int64_t sh, int H, const float* __restrict__ mean,
                                                        int8_t* __restrict__ out, float* __restrict__ scale_out,
-                                                       int64_t blk_cap) {
-  __shared__ float wmax[4];
+                                                       int64_t blk_cap, int halves) {
+  __shared__ float wmax[2][4];
   const int tid = threadIdx.x, c8 = tid & 15, h = blockIdx.y;
   const int64_t blk = blockIdx.x;
   SegInfo si;
@@ -108,7 +110,7 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
 #pragma unroll
   for (int j = 0; j < 8; ++j) mu[j] = mean ? mean[((int64_t)s * H + h) * kD + 8 * c8 + j] : 0.f;
   float xs[4][8];
-  float amax = 0.f;
+  float am[2] = {0.f, 0.f};  // per 32-row half
   const uint16_t* base = x + si.elem_base + h * sh + 8 * c8;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -119,19 +121,28 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         xs[i][j] = raw[j] - mu[j];  // K smoothing: one correctly rounded FP32 subtraction
-        amax = fmaxf(amax, fabsf(xs[i][j]));
+        am[i >> 1] = fmaxf(am[i >> 1], fabsf(xs[i][j]));
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) xs[i][j] = 0.f;
     }
   }
-  amax = wave_max(amax);
-  if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const float m = wave_max(am[f]);
+    if ((tid & 63) == 0) wmax[f][tid >> 6] = m;
+  }
   __syncthreads();
-  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const float scale = amax > 0.f ? amax / 127.0f : 0.f;
-  const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+#pragma unroll
+  for (int f = 0; f < 2; ++f) am[f] = fmaxf(fmaxf(wmax[f][0], wmax[f][1]), fmaxf(wmax[f][2], wmax[f][3]));
+  if (halves == 1) am[0] = am[1] = fmaxf(am[0], am[1]);
+  float scale[2], inv[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    scale[f] = am[f] > 0.f ? am[f] / 127.0f : 0.f;
+    inv[f] = am[f] > 0.f ? 127.0f / am[f] : 0.f;
+  }
   int8_t* tile = out + ((int64_t)h * blk_cap + blk) * kTileBytes;
   const int cbase = 8 * c8, g2 = cbase >> 6, u = (cbase & 63) >> 4, s0 = cbase & 15;
 #pragma unroll
@@ -140,14 +151,14 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float qv = rintf(xs[i][j] * inv);  // round half to even
+      float qv = rintf(xs[i][j] * inv[i >> 1]);  // round half to even
       qv = fminf(fmaxf(qv, -127.f), 127.f);
       w[j >> 2] |= ((uint32_t)((int)qv) & 0xffu) << (8 * (j & 3));
     }
     const int off = ((t * 4 + u) * 64 + g2 * 32 + ri) * 16 + s0;
     *reinterpret_cast<uint2*>(tile + off) = make_uint2(w[0], w[1]);
   }
-  if (tid == 0) scale_out[(int64_t)h * blk_cap + blk] = scale;
+  if (tid < halves) scale_out[((int64_t)h * blk_cap + blk) * halves + tid] = scale[tid];
 }
 
 // ---------------------------------------------------------------------------- V
@@ -223,10 +234,10 @@ hipError_t launch_quantize(const QuantLaunch& a, hipStream_t stream) {
                      a.k_mean, a.v_scale, vinv);
   if (a.q_blocks > 0)
     hipLaunchKernelGGL(quant_qk_kernel, dim3(a.q_blocks, a.H), dim3(256), 0, stream, a.q, a.gq, a.q_st, a.q_sh, a.H,
-                       (const float*)nullptr, a.q8, a.q_scale, a.qblk_cap);
+                       (const float*)nullptr, a.q8, a.q_scale, a.qblk_cap, 1 << a.q_scale_shift);
   if (a.k_blocks > 0) {
     hipLaunchKernelGGL(quant_qk_kernel, dim3(a.k_blocks, a.H), dim3(256), 0, stream, a.k, a.gk, a.k_st, a.k_sh, a.H,
-                       (const float*)a.k_mean, a.k8, a.k_scale, a.kblk_cap);
+                       (const float*)a.k_mean, a.k8, a.k_scale, a.kblk_cap, 1);
     hipLaunchKernelGGL(quant_v_kernel, dim3(a.k_blocks, a.H), dim3(256), 0, stream, a.v, a.gv, a.v_st, a.v_sh, a.H,
                        (const float*)vinv, a.v8, a.kblk_cap);
   }

@@ -38,7 +38,7 @@ def test_status_strings():
 def test_quant_query_sizes():
     s = B.sattn_quant_query(1, 37810, 37810, 32)
     assert s.qblk_cap == 37810 // 64 + 1 == 591
-    assert s.q_bytes == 32 * 591 * 8192 and s.q_scale_bytes == 32 * 591 * 4
+    assert s.q_bytes == 32 * 591 * 8192 and s.q_scale_bytes == 32 * 591 * 2 * 4  # room for 32-row scales
     assert s.k_mean_bytes == 32 * 128 * 4 and s.v_bytes == s.k_bytes
     v = B.sattn_quant_query(4, 47638, 47638, 24)
     assert v.kblk_cap == 47638 // 64 + 4
@@ -67,8 +67,8 @@ def test_capacity_bound_covers_every_segment_layout():
         assert all(ends[s] <= starts[s + 1] for s in range(len(lens) - 1))
 
 
-def _quant_struct(cap=100, ptr=FAKE):
-    return B.QKVQuant(ptr, ptr, ptr, ptr, ptr, ptr, ptr, cap, cap)
+def _quant_struct(cap=100, ptr=FAKE, rows=64):
+    return B.QKVQuant(ptr, ptr, ptr, ptr, ptr, ptr, ptr, cap, cap, rows)
 
 
 def _in(ptr=FAKE, sb=0, st=128, sh=128):
@@ -99,6 +99,8 @@ def test_quantize_validation():
     assert call(ws=None) == B.SATTN_EINVAL
     assert call(out=_quant_struct(cap=1)) == B.SATTN_ENOSPACE
     assert call(wsb=16) == B.SATTN_ENOSPACE
+    for rows in (1, 16, 48, 128, -32):
+        assert call(out=_quant_struct(rows=rows)) == B.SATTN_EINVAL
 
 
 def test_fwd_validation():
@@ -113,6 +115,7 @@ def test_fwd_validation():
     assert f(ctypes.byref(q), 1, 1, 64, 64, 128, 0.1, _out(st=4), None) == B.SATTN_EINVAL
     assert f(ctypes.byref(_quant_struct(cap=0)), 2, 1, 64, 64, 128, 0.1, _out(), None) == B.SATTN_ENOSPACE
     assert f(None, 1, 1, 64, 64, 128, 0.1, _out(), None) == B.SATTN_EINVAL
+    assert f(ctypes.byref(_quant_struct(rows=16)), 1, 1, 64, 64, 128, 0.1, _out(), None) == B.SATTN_EINVAL
     v = L.sattn_fwd_varlen
     assert v(ctypes.byref(q), FAKE, FAKE, 2, 100, 1, 128, 0.1, _out(), FAKE, 4, None) == B.SATTN_ENOSPACE
     assert v(ctypes.byref(q), None, FAKE, 2, 100, 1, 128, 0.1, _out(), FAKE, 1024, None) == B.SATTN_EINVAL

@@ -42,16 +42,16 @@ def _tensor_cu(cu):
     return torch.tensor(cu, dtype=torch.int32, device="cuda")
 
 
-def gpu_run(inp, sm_scale):
+def gpu_run(inp, sm_scale, q_scale_rows=64):
     """Quantize + forward on the GPU for a workload input dict; returns (quant, out)."""
     w = inp["workload"]
     dev = W.to_device(inp)
     if w.varlen:
         cq, ck = _tensor_cu(inp["cu_q"]), _tensor_cu(inp["cu_k"])
-        quant = B.sattn_quantize_qkv(dev["q"], dev["k"], dev["v"], cq, ck)
+        quant = B.sattn_quantize_qkv(dev["q"], dev["k"], dev["v"], cq, ck, q_scale_rows=q_scale_rows)
         out = B.sattn_fwd_varlen(quant, cq, ck, dev["q"].shape[0], sm_scale)
     else:
-        quant = B.sattn_quantize_qkv(dev["q"], dev["k"], dev["v"])
+        quant = B.sattn_quantize_qkv(dev["q"], dev["k"], dev["v"], q_scale_rows=q_scale_rows)
         Bn, Lq, H = dev["q"].shape[:3]
         out = B.sattn_fwd(quant, Bn, H, Lq, dev["k"].shape[1], sm_scale)
     torch.cuda.synchronize()
@@ -59,16 +59,16 @@ def gpu_run(inp, sm_scale):
 
 
 @functools.lru_cache(maxsize=8)
-def case(name):
+def case(name, q_scale_rows=64):
     """GPU results and oracle quantization of one workload (cached for the session)."""
     _need_gpu()
     w = W.get(name)
-    _say(f"[case] {name}: generate + GPU")
+    _say(f"[case] {name} (Q scale per {q_scale_rows} rows): generate + GPU")
     inp = W.make_inputs(w)
-    quant, out = gpu_run(inp, w.sm_scale)
+    quant, out = gpu_run(inp, w.sm_scale, q_scale_rows)
     _say(f"[case] {name}: oracle quantize")
     q64, k64, v64 = (W.packed_float64(inp[n]) for n in "qkv")
-    oq = O.quantize(q64, k64, v64, inp["cu_q"], inp["cu_k"])
+    oq = O.quantize(q64, k64, v64, inp["cu_q"], inp["cu_k"], q_rows=q_scale_rows)
     return dict(w=w, inp=inp, quant=quant, out=out, oq=oq)
 
 
@@ -143,6 +143,62 @@ def test_output_within_tolerance(name):
         else:
             got = out[si].numpy()
         _check_output(got[rows[si]].astype(np.float64), ref[si], f"{name} seg {si}")
+    assert torch.isfinite(c["out"].float()).all()
+
+
+# ---------------------------------------------------------------- per-warp (32-row) Q scales
+Q32_NAMES = ["fixed_q128_kv192", "ragged_b2_h16_l1000", "ragged_b2_h16_l2049", "varlen_h24_4seg"]
+
+
+@pytest.mark.parametrize("name", Q32_NAMES)
+def test_q32_quantized_buffers_bit_exact(name):
+    c = case(name, 32)
+    w, quant, oq, inp = c["w"], c["quant"], c["oq"], c["inp"]
+    qt, kt = quant.q.cpu().numpy(), quant.k.cpu().numpy()
+    qs = quant.q_scale.view(w.H, quant.qblk_cap, 2).cpu().numpy()
+    ks = quant.k_scale.cpu().numpy()
+    bq, bk = _blocks(inp["cu_q"], w), _blocks(inp["cu_k"], w)
+    for si, seg in enumerate(oq):
+        Lq, Lk = seg["q8"].shape[0], seg["k8"].shape[0]
+        nq, nk, n32 = -(-Lq // 64), -(-Lk // 64), -(-Lq // 32)
+        assert seg["q_scale"].shape[1] == n32
+        for h in range(w.H):
+            gq = B.untile_qk(qt[h, bq[si]:bq[si] + nq])
+            assert np.array_equal(gq[:Lq], seg["q8"][:, h, :].astype(np.int8)), f"q8 seg {si} head {h}"
+            assert not gq[Lq:].any(), "padding must be zero"
+            halves = qs[h, bq[si]:bq[si] + nq].reshape(-1)
+            assert np.array_equal(halves[:n32], seg["q_scale"][h].astype(np.float32)), f"q_scale seg {si} head {h}"
+            assert not halves[n32:].any(), "the scale of an empty half is 0"
+            gk = B.untile_qk(kt[h, bk[si]:bk[si] + nk])
+            assert np.array_equal(gk[:Lk], seg["k8"][:, h, :].astype(np.int8)), f"k8 seg {si} head {h}"
+            assert np.array_equal(ks[h, bk[si]:bk[si] + nk], seg["k_scale"][h].astype(np.float32))
+
+
+@pytest.mark.parametrize("name,seg,head", [("fixed_q128_kv192", 0, 0), ("ragged_b2_h16_l1000", 1, 9),
+                                           ("ragged_b2_h16_l2049", 0, 3)])
+def test_q32_scores_bit_exact(name, seg, head):
+    c = case(name, 32)
+    w = c["w"]
+    Bn, Lq, H = c["inp"]["q"].shape[:3]
+    Lk = c["inp"]["k"].shape[1]
+    acc, s, out = B.sattn_debug_scores(c["quant"], Bn, H, Lq, Lk, w.sm_scale, seg, head)
+    torch.cuda.synchronize()
+    r_acc, r_s = O.scores(c["oq"][seg], head, w.sm_scale)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), r_acc.astype(np.int64))
+    assert np.array_equal(s.cpu().numpy(), r_s.astype(np.float32))
+    assert torch.equal(out, c["out"])
+
+
+@pytest.mark.parametrize("name", Q32_NAMES)
+def test_q32_output_within_tolerance(name):
+    c = case(name, 32)
+    w, oq, inp = c["w"], c["oq"], c["inp"]
+    out = c["out"].float().cpu()
+    rows = {si: _sample_rows(seg["q8"].shape[0]) for si, seg in enumerate(oq)}
+    ref = O.attention(oq, w.sm_scale, rows=rows)
+    for si, (a, b) in enumerate(O.segments(inp["cu_q"])):
+        got = out[a:b].numpy() if w.varlen else out[si].numpy()
+        _check_output(got[rows[si]].astype(np.float64), ref[si], f"{name} (32-row Q scales) seg {si}")
     assert torch.isfinite(c["out"].float()).all()
 
 

@@ -112,6 +112,26 @@ def _e4m3_three_bits(x):
     return np.clip(_round_to_bits(x, 3, -9), -448.0, 448.0)
 
 
+def _scores_ignoring_q_rows(seg, h, sm_scale, rows=None):
+    q8, k8 = seg["q8"][:, h, :], seg["k8"][:, h, :]
+    rows = np.arange(q8.shape[0]) if rows is None else np.asarray(rows)
+    acc = q8[rows] @ k8.T
+    sig = O.block_sigma(seg["q_scale"][h], seg["k_scale"][h], O.sm_scale_log2(sm_scale))
+    sig_full = np.repeat(sig[np.minimum(rows // O.BLOCK, sig.shape[0] - 1)], O.BLOCK, axis=1)[:, :k8.shape[0]]
+    return acc, fl32(acc * sig_full)
+
+
+def _quantize_ignoring_q_rows(q, k, v, cu_q, cu_k, q_rows=None):
+    out = _REAL_QUANTIZE(q, k, v, cu_q, cu_k)
+    for seg in out:
+        seg["q_rows"] = q_rows or O.BLOCK
+        if q_rows == 32:  # one 64-row scale reported twice
+            seg["q_scale"] = np.repeat(seg["q_scale"], 2, axis=1)[:, :-(-seg["q8"].shape[0] // 32)]
+    return out
+
+
+_REAL_QUANTIZE = O.quantize
+
 PINS_ATTN = [
     lambda: P.test_identity_rounding_equals_textbook_softmax(64),
     lambda: P.test_identity_rounding_equals_textbook_softmax(7),
@@ -131,6 +151,13 @@ PINS_QUANT = [
     P.test_grid_exact_case_equals_brute_force,
     P.test_quantized_program_tracks_exact_attention,
     P.test_pages_shape_facts,
+]
+
+PINS_Q32 = [
+    P.test_q32_scales_are_per_32_rows_and_partial_tail,
+    P.test_q32_doubling_one_half_doubles_only_its_scores,
+    P.test_q32_equals_q64_when_halves_share_their_amax,
+    P.test_q32_program_tracks_exact_attention,
 ]
 
 MUTANTS = {
@@ -159,6 +186,10 @@ MUTANTS = {
     "epilogue without v_scale": (lambda mp: mp.setattr(O, "attention", _attention_variant(drop_v_scale=True)),
                                  PINS_ATTN),
     "E4M3 with three significant bits": (lambda mp: mp.setattr(O, "e4m3", _e4m3_three_bits), PINS_ATTN + PINS_QUANT),
+    "32-row Q scales read with the 64-row block index": (lambda mp: mp.setattr(O, "scores", _scores_ignoring_q_rows),
+                                                          PINS_Q32),
+    "32-row Q scales computed over 64 rows": (lambda mp: mp.setattr(O, "quantize", _quantize_ignoring_q_rows),
+                                             PINS_Q32),
 }
 
 

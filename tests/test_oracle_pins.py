@@ -259,6 +259,68 @@ def test_rows_subset_matches_full():
     assert np.array_equal(sub, full[rows])
 
 
+# ---------------------------------------------------------------- per-warp (32-row) Q scales
+def test_q32_scales_are_per_32_rows_and_partial_tail():
+    rng = np.random.default_rng(30)
+    x = fl32(rng.standard_normal((70, 2, 128)))
+    x[40, 1, 7] = 50.0  # rows 32..63 of head 1 only
+    x[69, 0, 2] = -80.0  # the 6-row tail block of head 0 only
+    codes, scales = O.quantize_int8_blocks(x, 32)
+    assert scales.shape == (2, 3)
+    assert scales[1, 1] == fl32(50.0 / 127.0) and scales[0, 2] == fl32(80.0 / 127.0)
+    for h in range(2):
+        for b, (a, e) in enumerate([(0, 32), (32, 64), (64, 70)]):
+            assert scales[h, b] == fl32(np.max(np.abs(x[a:e, h])) / 127.0)
+    # rows 0..31 keep the codes of their own scale: the outlier at row 40 does not touch them
+    c0, _ = O.quantize_int8_blocks(x[:32], 32)
+    assert np.array_equal(codes[:32], c0)
+
+
+def test_q32_doubling_one_half_doubles_only_its_scores():
+    """Q rows 32..63 times 2 (exact in BF16): with 32-row scales their codes stay, their
+    scale doubles, so their scores double exactly and the other rows' scores do not move.
+    With one scale per 64 rows the codes of rows 0..31 would change."""
+    rng = np.random.default_rng(31)
+    L, H, D = 100, 2, 128
+    q, k, v = (_bf16_randn(rng, (L, H, D)) for _ in range(3))
+    q2 = q.copy()
+    q2[32:64] *= 2.0
+    a = O.quantize(q, k, v, [0, L], [0, L], q_rows=32)[0]
+    b = O.quantize(q2, k, v, [0, L], [0, L], q_rows=32)[0]
+    assert np.array_equal(a["q8"], b["q8"])
+    assert np.array_equal(b["q_scale"][:, 1], 2.0 * a["q_scale"][:, 1])
+    assert np.array_equal(np.delete(b["q_scale"], 1, axis=1), np.delete(a["q_scale"], 1, axis=1))
+    for h in range(H):
+        _, sa = O.scores(a, h, D ** -0.5)
+        _, sb = O.scores(b, h, D ** -0.5)
+        assert np.array_equal(sb[32:64], 2.0 * sa[32:64])
+        assert np.array_equal(np.delete(sb, np.s_[32:64], axis=0), np.delete(sa, np.s_[32:64], axis=0))
+    c64 = O.quantize(q2, k, v, [0, L], [0, L])[0]
+    assert not np.array_equal(c64["q8"][:32], a["q8"][:32])
+
+
+def test_q32_equals_q64_when_halves_share_their_amax():
+    rng = np.random.default_rng(32)
+    L, H, D = 128, 2, 128
+    q, k, v = (_bf16_randn(rng, (L, H, D)) for _ in range(3))
+    q[0::32, :, 5] = 9.0  # the largest |q| of every 32-row half, per head: equal halves
+    s32 = O.quantize(q, k, v, [0, L], [0, L], q_rows=32)[0]
+    s64 = O.quantize(q, k, v, [0, L], [0, L])[0]
+    assert np.array_equal(s32["q8"], s64["q8"])
+    assert np.array_equal(s32["q_scale"], np.repeat(s64["q_scale"], 2, axis=1))
+    assert np.array_equal(O.attention([s32], D ** -0.5), O.attention([s64], D ** -0.5))
+
+
+def test_q32_program_tracks_exact_attention():
+    rng = np.random.default_rng(33)
+    L, H, D = 512, 2, 128
+    q, k, v = (_bf16_randn(rng, (L, H, D)) for _ in range(3))
+    k = k + bf16(rng.standard_normal((H, D)) * 2.0)[None]
+    got = O.attention(O.quantize(q, k, v, [0, L], [0, L], q_rows=32), D ** -0.5)
+    ref = O.softmax_attention_exact(q, k, v, D ** -0.5)
+    assert O.rel_l2(got, ref) <= 5e-2
+
+
 # ---------------------------------------------------------------- the pages' shape facts
 def test_pages_shape_facts():
     facts = json.load(open(GOLDEN))["facts"]
