@@ -1,6 +1,6 @@
 """Throughput of the quantized attention hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--fused-q]
 
 A step is one pass of the whole path over one batch of synthetic input already resident
 in HBM: sattn_quantize_qkv (K statistics, INT8 Q/K tiles, E4M3 V tiles) followed by
@@ -11,6 +11,11 @@ B=1, H=32, L=37,810 packed tokens, D=128, Q/K/V projection-strided slices of one
 runs on; its algorithmic operation count over that time, against the 5.0 POP/s dense
 INT8/FP8 MFMA peak, is the roofline entry.  The CPU baseline times the FP64 oracle on a
 bounded sample of the same workload and extrapolates linearly.
+
+--fused-q times the other form of the same path: sattn_quantize_qkv for K and V only, then
+sattn_fwd_fused, which quantizes Q inside the attention launch from the BF16 view (the
+outputs are bit-identical).  Its roofline entry carries no traffic figure: the committed
+counter summary is for the two-pass launch.
 """
 import argparse
 import hashlib
@@ -106,6 +111,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="h3_video_l37810")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused-q", action="store_true",
+                    help="step = K/V-only quantization + sattn_fwd_fused (Q prepared in the attention launch)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run N plain 1 GiB device copies (counter calibration) and exit")
     args = ap.parse_args()
@@ -136,7 +143,7 @@ def main():
     q, k, v = dev["q"], dev["k"], dev["v"]
     Bn, Lq, H = q.shape[:3]
     Lk = k.shape[1]
-    quant = B.alloc_quantized(Bn, Bn * Lq, Bn * Lk, H)
+    quant = B.alloc_quantized(Bn, Bn * Lq, Bn * Lk, H, with_q=not args.fused_q)
     out = torch.empty((Bn, Lq, H, 128), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
 
@@ -146,7 +153,10 @@ def main():
         B.sattn_quantize_qkv(q, k, v, out=quant, stream=stream)
         if ev:
             ev[1].record(stream)
-        B.sattn_fwd(quant, Bn, H, Lq, Lk, w.sm_scale, out=out, stream=stream)
+        if args.fused_q:
+            B.sattn_fwd_fused(quant, q, w.sm_scale, Lk=Lk, out=out, stream=stream)
+        else:
+            B.sattn_fwd(quant, Bn, H, Lq, Lk, w.sm_scale, out=out, stream=stream)
         if ev:
             ev[2].record(stream)
 
@@ -168,10 +178,12 @@ def main():
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
     quant_avg = sum(quant_ms) / len(quant_ms)
     achieved = ops / (fwd_avg * 1e-3) / 1e12
-    traffic = measured_traffic(w.name)
+    traffic = None if args.fused_q else measured_traffic(w.name)
     # algorithmic HBM bytes of the quantization pass: Q read once (2D) and written as INT8
     # (D); K and V read twice each (statistics, then quantization: 8D) and written once (2D)
-    quant_bytes = H * Bn * (3 * 128 * Lq + 10 * 128 * Lk)
+    quant_bytes = H * Bn * ((0 if args.fused_q else 3 * 128 * Lq) + 10 * 128 * Lk)
+    step_name = ("sattn_quantize_qkv (K, V) + sattn_fwd_fused" if args.fused_q
+                 else "sattn_quantize_qkv + sattn_fwd")
     result = {
         "metric": "attention TOPS (4*Lq*Lkv*D*H/s) at L=37,810 D=128; % of MFMA peak",
         "value": ops / (ms_per_step * 1e-3) / 1e12,
@@ -186,7 +198,7 @@ def main():
         "dtype": "int8 (QK) + fp8 e4m3 (PV), fp32 softmax",
         "data": "synthetic (seeded N(0,1) BF16, per-channel K bias N(0,2))",
         "config": {"workload": w.name, "B": Bn, "H": H, "Lq": Lq, "Lk": Lk, "D": 128,
-                   "layout": w.layout, "step": "sattn_quantize_qkv + sattn_fwd"},
+                   "layout": w.layout, "step": step_name},
         "roofline": {
             "bound": "mfma",
             "kernel": "attn_fwd_kernel",

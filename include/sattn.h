@@ -152,6 +152,9 @@ SATTN_API sattn_status sattn_quant_query(int nseg, int64_t total_q, int64_t tota
  * `workspace` must hold quant_workspace_bytes from sattn_quant_query (16-byte aligned);
  * it is scratch: its contents are undefined after the call.  Returns SATTN_ENOSPACE when
  * a capacity in `out` or workspace_bytes is too small.
+ *
+ * K and V only: with out->q and out->q_scale both NULL, the Q step is skipped and the q
+ * view is not read (it may be NULL); this is the preparation sattn_fwd_fused needs.
  */
 SATTN_API sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in v, int nseg, int H, int D,
                                 int64_t Lq, int64_t Lk, const int32_t* cu_seqlens_q,
@@ -197,6 +200,31 @@ SATTN_API sattn_status sattn_fwd_varlen(const sattn_qkv_quant* qkv, const int32_
 SATTN_API sattn_status sattn_debug_scores(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D,
                                 float sm_scale, int seg, int head, int32_t* acc_out, float* s_out,
                                 sattn_bf16_out o, void* stream);
+
+/*
+ * sattn_fwd_fused — the forward with the Q preparation fused into the attention launch
+ * (the roadmap page's "Phase 4" items on fusing preparation and consuming the projection-
+ * strided input): each workgroup reads its query rows straight from the BF16 view `q`
+ * (same strides and alignment rules as sattn_quantize_qkv's views) and quantizes them in
+ * registers with exactly the arithmetic of sattn_quantize_qkv's Q step (amax per 64-token
+ * block, or per 32 rows when kv->q_scale_rows = 32; fl32 scale and reciprocal; RNE codes
+ * in [-127, 127]), so the output equals sattn_quantize_qkv + sattn_fwd(_varlen) bit for
+ * bit.  No INT8 Q is written.  kv holds K and V as written by sattn_quantize_qkv (its q
+ * and q_scale are not read and may be NULL).
+ *
+ *   dense  (cu_seqlens_q == cu_seqlens_k == NULL): nseg segments of Lq queries and Lk
+ *          keys; q and o are [nseg, Lq, H, D] views; workspace may be NULL.
+ *   varlen (both non-NULL): the cu_seqlens arrays given to sattn_quantize_qkv; Lq is the
+ *          number of packed query tokens the q and o views hold, Lk the packed key
+ *          tokens; workspace: fwd_workspace_bytes (16-byte aligned), scratch.
+ *
+ * Errors as sattn_fwd / sattn_fwd_varlen; SATTN_ENOSPACE if kv->kblk_cap cannot hold the
+ * key blocks or workspace_bytes is too small.
+ */
+SATTN_API sattn_status sattn_fwd_fused(const sattn_qkv_quant* kv, sattn_bf16_in q, const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_k, int nseg, int H, int64_t Lq, int64_t Lk, int D,
+                             float sm_scale, sattn_bf16_out o, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* Static, human-readable name of a status code. */
 SATTN_API const char* sattn_status_string(sattn_status s);

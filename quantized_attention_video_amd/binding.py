@@ -17,7 +17,7 @@ D = 128
 
 SATTN_OK, SATTN_EINVAL, SATTN_EUNSUPPORTED, SATTN_ENOSPACE, SATTN_EHIP = range(5)
 EXPORTED = ("sattn_quant_query", "sattn_quantize_qkv", "sattn_fwd", "sattn_fwd_varlen", "sattn_debug_scores",
-            "sattn_status_string")
+            "sattn_fwd_fused", "sattn_status_string")
 
 
 class SattnError(RuntimeError):
@@ -69,6 +69,8 @@ def lib():
                                        ctypes.c_size_t, vp]
         L.sattn_debug_scores.argtypes = [ctypes.POINTER(QKVQuant), i32, i32, i32, i32, i32, f32, i32, i32, vp, vp,
                                          BF16Out, vp]
+        L.sattn_fwd_fused.argtypes = [ctypes.POINTER(QKVQuant), BF16In, vp, vp, i32, i32, i64, i64, i32, f32,
+                                      BF16Out, vp, ctypes.c_size_t, vp]
         L.sattn_status_string.argtypes = [i32]
         L.sattn_status_string.restype = ctypes.c_char_p
         for name in EXPORTED[:-1]:
@@ -132,20 +134,21 @@ class Quantized:
     q_scale_rows: int = 64  # query rows per Q scale: 64 or 32 (q_scale is [H, qblk_cap * 64 / rows])
 
     def struct(self):
-        return QKVQuant(self.q.data_ptr(), self.q_scale.data_ptr(), self.k.data_ptr(), self.k_scale.data_ptr(),
+        return QKVQuant(_ptr(self.q), _ptr(self.q_scale), self.k.data_ptr(), self.k_scale.data_ptr(),
                         self.k_mean.data_ptr(), self.v.data_ptr(), self.v_scale.data_ptr(), self.qblk_cap,
                         self.kblk_cap, self.q_scale_rows)
 
 
-def alloc_quantized(nseg, total_q, total_k, H, device="cuda", q_scale_rows=64):
-    """Allocate (uninitialised) quantized buffers sized by sattn_quant_query."""
+def alloc_quantized(nseg, total_q, total_k, H, device="cuda", q_scale_rows=64, with_q=True):
+    """Allocate (uninitialised) quantized buffers sized by sattn_quant_query.  with_q=False
+    leaves out the INT8 Q buffers (K/V only, for sattn_fwd_fused)."""
     if q_scale_rows not in (32, 64):
         raise ValueError("q_scale_rows must be 32 or 64")
     s = sattn_quant_query(nseg, total_q, total_k, H)
     e = dict(device=device)
     return Quantized(
-        q=torch.empty((H, s.qblk_cap, 8192), dtype=torch.int8, **e),
-        q_scale=torch.empty((H, s.qblk_cap * (64 // q_scale_rows)), dtype=torch.float32, **e),
+        q=torch.empty((H, s.qblk_cap, 8192), dtype=torch.int8, **e) if with_q else None,
+        q_scale=torch.empty((H, s.qblk_cap * (64 // q_scale_rows)), dtype=torch.float32, **e) if with_q else None,
         k=torch.empty((H, s.kblk_cap, 8192), dtype=torch.int8, **e),
         k_scale=torch.empty((H, s.kblk_cap), dtype=torch.float32, **e),
         k_mean=torch.empty((nseg, H, D), dtype=torch.float32, **e),
@@ -173,7 +176,8 @@ def sattn_quantize_qkv(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, out=None, 
     if out is None:
         out = alloc_quantized(nseg, total_q, total_k, H, device=q.device, q_scale_rows=q_scale_rows)
     st = out.struct()
-    _check(lib().sattn_quantize_qkv(_view(q, BF16In), _view(k, BF16In), _view(v, BF16In), nseg, H, D, Lq, Lk,
+    qv = _view(q, BF16In) if out.q is not None else BF16In(0, 0, 0, 0)
+    _check(lib().sattn_quantize_qkv(qv, _view(k, BF16In), _view(v, BF16In), nseg, H, D, Lq, Lk,
                                     _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), ctypes.byref(st),
                                     out.workspace.data_ptr(), out.workspace.numel(), _stream(stream)),
            "sattn_quantize_qkv")
@@ -187,6 +191,45 @@ def sattn_fwd(quant, B, H, Lq, Lk, sm_scale, out=None, stream=None):
     st = quant.struct()
     _check(lib().sattn_fwd(ctypes.byref(st), B, H, Lq, Lk, D, float(sm_scale), _view(out, BF16Out),
                            _stream(stream)), "sattn_fwd")
+    return out
+
+
+def sattn_quantize_kv(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, stream=None, q_scale_rows=64):
+    """K/V-only preparation for sattn_fwd_fused (Q buffers absent; the q view only gives
+    the problem's query geometry and is not read)."""
+    varlen = cu_seqlens_q is not None
+    if varlen:
+        nseg, H = cu_seqlens_q.numel() - 1, q.shape[1]
+        total_q, total_k = q.shape[0], k.shape[0]
+    else:
+        nseg, H = q.shape[0], q.shape[2]
+        total_q, total_k = nseg * q.shape[1], nseg * k.shape[1]
+    out = alloc_quantized(nseg, total_q, total_k, H, device=k.device, q_scale_rows=q_scale_rows, with_q=False)
+    return sattn_quantize_qkv(q, k, v, cu_seqlens_q, cu_seqlens_k, out=out, stream=stream)
+
+
+def sattn_fwd_fused(kv, q, sm_scale, cu_seqlens_q=None, cu_seqlens_k=None, Lk=None, out=None, workspace=None,
+                    stream=None):
+    """Forward with the Q preparation in the attention launch.  Dense: q is a [B, Lq, H, D]
+    view and Lk the keys per segment; varlen: q is packed [T, H, D] and Lk the packed key
+    tokens.  Returns (or fills) the BF16 output shaped like q."""
+    if Lk is None:
+        raise ValueError("Lk (keys per segment, or packed key tokens) is required")
+    varlen = cu_seqlens_q is not None
+    if varlen:
+        nseg, Lq, H = cu_seqlens_q.numel() - 1, q.shape[0], q.shape[1]
+        if workspace is None:
+            workspace = fwd_workspace(nseg, device=q.device)
+        ws, wsb = workspace.data_ptr(), workspace.numel()
+    else:
+        nseg, Lq, H = q.shape[0], q.shape[1], q.shape[2]
+        ws, wsb = None, 0
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    st = kv.struct()
+    _check(lib().sattn_fwd_fused(ctypes.byref(st), _view(q, BF16In), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), nseg, H,
+                                 Lq, Lk, D, float(sm_scale), _view(out, BF16Out), ws, wsb, _stream(stream)),
+           "sattn_fwd_fused")
     return out
 
 

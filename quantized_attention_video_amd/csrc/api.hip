@@ -39,10 +39,12 @@ QuantWs quant_ws(int nseg, int H) {
 
 size_t fwd_ws(int nseg) { return align_up((size_t)nseg * 4) + align_up(((size_t)nseg + 1) * 4); }
 
-bool quant_bufs_ok(const sattn_qkv_quant* b) {
-  return b && b->q && b->q_scale && b->k && b->k_scale && b->k_mean && b->v && b->v_scale && aligned16(b->q) &&
-         aligned16(b->k) && aligned16(b->v) && b->qblk_cap >= 0 && b->kblk_cap >= 0 &&
-         (b->q_scale_rows == 0 || b->q_scale_rows == 32 || b->q_scale_rows == 64);
+// need_q: the Q buffers take part (false for the fused-Q forward and K/V-only quantization).
+bool quant_bufs_ok(const sattn_qkv_quant* b, bool need_q = true) {
+  if (b == nullptr) return false;
+  if (need_q && (b->q == nullptr || b->q_scale == nullptr || !aligned16(b->q) || b->qblk_cap < 0)) return false;
+  return b->k && b->k_scale && b->k_mean && b->v && b->v_scale && aligned16(b->k) && aligned16(b->v) &&
+         b->kblk_cap >= 0 && (b->q_scale_rows == 0 || b->q_scale_rows == 32 || b->q_scale_rows == 64);
 }
 
 // log2(64 / q_scale_rows): Q scales per 64-token block, as a shift.
@@ -93,14 +95,16 @@ sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in 
   if (D != kD || nseg > 65535 || H > 65535) return SATTN_EUNSUPPORTED;  // grid y/z extents
   const bool varlen = cu_seqlens_q != nullptr;
   if ((cu_seqlens_k != nullptr) != varlen) return SATTN_EINVAL;
-  if (!view_ok(q.ptr, q.stride_b, q.stride_t, q.stride_h, !varlen) ||
+  // Q buffers both NULL: K and V only (for sattn_fwd_fused, which quantizes Q itself)
+  const bool do_q = out == nullptr || out->q != nullptr || out->q_scale != nullptr;
+  if ((do_q && !view_ok(q.ptr, q.stride_b, q.stride_t, q.stride_h, !varlen)) ||
       !view_ok(k.ptr, k.stride_b, k.stride_t, k.stride_h, !varlen) ||
       !view_ok(v.ptr, v.stride_b, v.stride_t, v.stride_h, !varlen))
     return SATTN_EINVAL;
-  if (!quant_bufs_ok(out) || workspace == nullptr || !aligned16(workspace)) return SATTN_EINVAL;
+  if (!quant_bufs_ok(out, do_q) || workspace == nullptr || !aligned16(workspace)) return SATTN_EINVAL;
   const int64_t total_q = varlen ? Lq : (int64_t)nseg * Lq;
   const int64_t total_k = varlen ? Lk : (int64_t)nseg * Lk;
-  if (out->qblk_cap < total_q / 64 + nseg || out->kblk_cap < total_k / 64 + nseg) return SATTN_ENOSPACE;
+  if ((do_q && out->qblk_cap < total_q / 64 + nseg) || out->kblk_cap < total_k / 64 + nseg) return SATTN_ENOSPACE;
   const QuantWs ws = quant_ws(nseg, H);
   if (workspace_bytes < ws.total) return SATTN_ENOSPACE;
 
@@ -116,7 +120,7 @@ sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in 
   a.v_st = v.stride_t; a.v_sh = v.stride_h;
   a.nseg = nseg;
   a.H = H;
-  a.q_blocks = varlen ? out->qblk_cap : nseg * ceil64(Lq);
+  a.q_blocks = !do_q ? 0 : varlen ? out->qblk_cap : nseg * ceil64(Lq);
   a.k_blocks = varlen ? out->kblk_cap : nseg * ceil64(Lk);
   a.q8 = out->q; a.q_scale = out->q_scale;
   a.k8 = out->k; a.k_scale = out->k_scale; a.k_mean = out->k_mean;
@@ -131,10 +135,10 @@ sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in 
 }
 
 static sattn_status fwd_common(const sattn_qkv_quant* qkv, int H, int D, float sm_scale, sattn_bf16_out o,
-                               bool dense) {
+                               bool dense, bool need_q = true) {
   if (H < 1) return SATTN_EINVAL;
   if (D != kD) return SATTN_EUNSUPPORTED;
-  if (!quant_bufs_ok(qkv)) return SATTN_EINVAL;
+  if (!quant_bufs_ok(qkv, need_q)) return SATTN_EINVAL;
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return SATTN_EINVAL;
   if (!view_ok(o.ptr, o.stride_b, o.stride_t, o.stride_h, dense)) return SATTN_EINVAL;
   return SATTN_OK;
@@ -219,6 +223,52 @@ sattn_status sattn_fwd_varlen(const sattn_qkv_quant* qkv, const int32_t* cu_seql
   if (grid > 0x7fffffff) return SATTN_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_plan(cu_seqlens_q, cu_seqlens_k, nseg, q_clip, k_clip, order, tpref, s) != hipSuccess) return SATTN_EHIP;
+  return launch_attention(p, grid, false, s) == hipSuccess ? SATTN_OK : SATTN_EHIP;
+}
+
+sattn_status sattn_fwd_fused(const sattn_qkv_quant* kv, sattn_bf16_in q, const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_k, int nseg, int H, int64_t Lq, int64_t Lk, int D,
+                             float sm_scale, sattn_bf16_out o, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (nseg < 1 || Lq < 0 || Lk < 0) return SATTN_EINVAL;
+  const bool varlen = cu_seqlens_q != nullptr;
+  if ((cu_seqlens_k != nullptr) != varlen) return SATTN_EINVAL;
+  sattn_status st = fwd_common(kv, H, D, sm_scale, o, !varlen, false);
+  if (st != SATTN_OK) return st;
+  if (!view_ok(q.ptr, q.stride_b, q.stride_t, q.stride_h, !varlen)) return SATTN_EINVAL;
+  if (varlen && (workspace == nullptr || !aligned16(workspace))) return SATTN_EINVAL;
+  if (varlen && workspace_bytes < fwd_ws(nseg)) return SATTN_ENOSPACE;
+  if (kv->kblk_cap < nseg || (!varlen && kv->kblk_cap < (int64_t)nseg * ceil64(Lk))) return SATTN_ENOSPACE;
+  const int64_t k_clip = varlen ? (Lk < clip_for_cap(kv->kblk_cap, nseg) ? Lk : clip_for_cap(kv->kblk_cap, nseg))
+                                : Lk;
+  AttnParams p;
+  memset(&p, 0, sizeof(p));
+  p.k8 = kv->k; p.k_scale = kv->k_scale;
+  p.v8 = kv->v; p.v_scale = kv->v_scale;
+  p.kblk_cap = kv->kblk_cap;
+  p.H = H; p.nseg = nseg;
+  p.gq = SegGeom{cu_seqlens_q, nseg, Lq, varlen ? 0 : o.stride_b};
+  p.gk = SegGeom{cu_seqlens_k, nseg, k_clip, 0};
+  p.c32 = log2e_scale(sm_scale);
+  p.o = static_cast<uint16_t*>(o.ptr);
+  p.o_st = o.stride_t; p.o_sh = o.stride_h;
+  p.dump_seg = -1; p.dump_head = -1;
+  p.q_scale_shift = q_scale_shift(kv);
+  p.max_kblocks = ceil64(k_clip);
+  p.qbf = static_cast<const uint16_t*>(q.ptr);
+  p.qb_sb = q.stride_b; p.qb_st = q.stride_t; p.qb_sh = q.stride_h;
+  const int qpw = attn_queries_per_wg();
+  const int64_t grid = varlen ? 8 * (int64_t)((H + 7) / 8) * (Lq / qpw + nseg + 1)
+                              : 8 * (int64_t)((H + 7) / 8) * nseg * ((ceil64(Lq) * 64 + qpw - 1) / qpw);
+  if (grid > 0x7fffffff) return SATTN_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (varlen) {
+    p.order = static_cast<int32_t*>(workspace);
+    p.tpref = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align_up((size_t)nseg * 4));
+    if (launch_plan(cu_seqlens_q, cu_seqlens_k, nseg, Lq, k_clip, const_cast<int32_t*>(p.order),
+                    const_cast<int32_t*>(p.tpref), s) != hipSuccess)
+      return SATTN_EHIP;
+  }
   return launch_attention(p, grid, false, s) == hipSuccess ? SATTN_OK : SATTN_EHIP;
 }
 

@@ -112,6 +112,7 @@ __shared__ __attribute__((aligned(16))) uint8_t g_qop[kQInLds ? kWaves : 1][kQIn
 // return out of order on the counter that LDS reads share.
 constexpr int kKsLds = 2048;
 __shared__ float g_ks[kKsLds];
+__shared__ float g_qamax[kWaves];  // fused Q preparation: each wave's 32-row amax
 constexpr int kChunksPerTile = kTileBytes / 16 / (kLoaderWaves * 64);  // per loader lane
 static_assert(kChunksPerTile * kLoaderWaves * 64 * 16 == kTileBytes, "tile split");
 
@@ -444,7 +445,30 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   c.qlds = g_qop[kQInLds ? wave : 0];
 #pragma unroll
   for (int u = 0; u < 4; ++u) c.qop[u] = v4i{0, 0, 0, 0};
-  if (c.active) {
+  // Fused Q preparation (sattn_fwd_fused): lane g*32 + i holds token 32*hq + i of the
+  // wave's 64-row block, channels 64g .. 64g+63, as BF16; the block amax goes through LDS
+  // to the sibling wave (one 64-row scale) unless each wave has its own 32-row scale.
+  const bool fused_q = p.qbf != nullptr;
+  uint4 qraw[8];
+  float qamax = 0.f;
+  if (fused_q) {
+    SegGeom gqin = p.gq;
+    gqin.stride_b = p.qb_sb;
+    const SegInfo qin = seg_info(gqin, s, p.qb_st);
+    const int64_t row = qb * kBlk + hq * 32 + (lane & 31);
+    const uint16_t* src = p.qbf + qin.elem_base + row * p.qb_st + (int64_t)h * p.qb_sh + 64 * c.g;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      qraw[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (c.active && row < qin.len) qraw[j] = *reinterpret_cast<const uint4*>(src + 8 * j);
+      float x[8];
+      unpack8(qraw[j], x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qamax = fmaxf(qamax, fabsf(x[i]));
+    }
+    qamax = wave_max(qamax);  // the wave's 32 rows
+    if (lane == 0) g_qamax[wave] = qamax;
+  } else if (c.active) {
     const int8_t* qt_ptr = p.q8 + ((int64_t)h * p.qblk_cap + qi.blk0 + qb) * kTileBytes;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -492,8 +516,30 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   if (nkb > 2) issue_tile(c, c.kg, 2, kslot<2>());
   if (nkb > 0) issue_tile(c, c.vg, 0, vslot<0>());
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  barrier();  // Q, K(0), the K scales and the zeroed V slot visible
+  barrier();  // Q, K(0), the K scales, the Q row maxima and the zeroed V slot visible
   if constexpr (KSL) c.ks_next = nkb > 0 ? g_ks[0] : 0.f;
+  if (fused_q && c.active) {  // the quantizer's arithmetic: fl32 scale, RNE codes in [-127, 127]
+    const float amax = p.q_scale_shift ? qamax : fmaxf(qamax, g_qamax[wave ^ 1]);
+    const float scale = amax > 0.f ? amax / 127.0f : 0.f;
+    const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {  // word w of operand u: channels 64g + 16u + 4w .. +3
+        float x[8];
+        unpack8(qraw[2 * u + (w >> 1)], x);
+        uint32_t word = 0u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          float qv = rintf(x[4 * (w & 1) + b] * inv);
+          qv = fminf(fmaxf(qv, -127.f), 127.f);
+          word |= ((uint32_t)((int)qv) & 0xffu) << (8 * b);
+        }
+        c.qop[u][w] = (int)word;
+      }
+    }
+    c.sig_q = scale * p.c32;
+  }
   if (nkb > 0) {
     qk_tile(acc[0], kslot<0>(), c.qop, c.qlds, lane, 0);
     qk_tile(acc[1], kslot<0>(), c.qop, c.qlds, lane, 1);

@@ -50,6 +50,8 @@ struct AttnParams {
   int64_t dump_lk;
   int64_t max_kblocks;  // bound on any segment's key blocks (selects the K-scale path)
   int q_scale_shift;    // Q scales per 64-token block: 1 << q_scale_shift (1 or 2)
+  const uint16_t* qbf;  // BF16 Q view quantized in the kernel (sattn_fwd_fused), else nullptr
+  int64_t qb_sb, qb_st, qb_sh;  // its batch, token and head element strides
 };
 
 int stats_chunks(int nseg, int H);

@@ -202,6 +202,37 @@ def test_q32_output_within_tolerance(name):
     assert torch.isfinite(c["out"].float()).all()
 
 
+# ---------------------------------------------------------------- Q preparation fused into the forward
+@pytest.mark.parametrize("name,rows", [("fixed_q128_kv192", 64), ("dense_h8_l4096", 64), ("ragged_b2_h16_l1000", 64),
+                                       ("ragged_b2_h16_l2049", 32), ("varlen_h24_4seg", 64), ("varlen_h24_4seg", 32),
+                                       ("h3_video_l37810", 64)])
+def test_fused_q_forward_equals_two_pass(name, rows):
+    """sattn_fwd_fused (Q quantized inside the attention launch, read from the BF16 view,
+    projection-strided for the video layout) gives the two-pass output bit for bit, and
+    the K/V-only preparation writes the same K/V buffers as the full one."""
+    c = case(name, rows)
+    w, inp, quant = c["w"], c["inp"], c["quant"]
+    dev = W.to_device(inp)
+    _say(f"[fused] {name}: K/V-only quantize + fused forward")
+    if w.varlen:
+        cq, ck = _tensor_cu(inp["cu_q"]), _tensor_cu(inp["cu_k"])
+        kv = B.sattn_quantize_kv(dev["q"], dev["k"], dev["v"], cq, ck, q_scale_rows=rows)
+        out = B.sattn_fwd_fused(kv, dev["q"], w.sm_scale, cq, ck, Lk=dev["k"].shape[0])
+    else:
+        kv = B.sattn_quantize_kv(dev["q"], dev["k"], dev["v"], q_scale_rows=rows)
+        out = B.sattn_fwd_fused(kv, dev["q"], w.sm_scale, Lk=dev["k"].shape[1])
+    torch.cuda.synchronize()
+    assert kv.q is None and kv.q_scale is None
+    for n in ("k_mean", "v_scale"):
+        assert torch.equal(getattr(kv, n), getattr(quant, n)), n
+    bk = _blocks(inp["cu_k"], w)  # capacity blocks beyond the segments are never written
+    for si, (a, b) in enumerate(O.segments(inp["cu_k"])):
+        blk = slice(bk[si], bk[si] + -(-(b - a) // 64))
+        for n in ("k", "k_scale", "v"):
+            assert torch.equal(getattr(kv, n)[:, blk], getattr(quant, n)[:, blk]), f"{n} seg {si}"
+    assert torch.equal(out, c["out"])
+
+
 def test_varlen_equals_per_segment_dense():
     _need_gpu()
     rng = torch.Generator().manual_seed(7)
