@@ -57,7 +57,8 @@ def measured_traffic(workload):
 
 def _head_slice(seg, n):
     """The first n heads of one segment of the oracle's quantized output."""
-    return {k: (v[:, :n] if k in ("q8", "k8", "v8", "v8val") else v[:n]) for k, v in seg.items()}
+    return {k: (v[:, :n] if k in ("q8", "k8", "v8", "v8val") else v[:n] if hasattr(v, "shape") else v)
+            for k, v in seg.items()}
 
 
 def cpu_baseline(w, inp, att_heads=8, rows=1024):

@@ -1,0 +1,34 @@
+"""Host-side pieces of bench.py (no GPU): the CPU baseline on a small workload, the
+traffic-summary lookup, and the refusal of more than one GPU."""
+import os
+import subprocess
+import sys
+
+import bench
+from quantized_attention_video_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_cpu_baseline_small_sample():
+    w = W.get("fixed_q128_kv192")
+    r = bench.cpu_baseline(w, W.make_inputs(w), att_heads=1, rows=64)
+    assert r["kind"] == "oracle" and r["unit"] == "TOPS" and r["value"] > 0 and r["cores"] >= 1
+    assert "extrapolated" in r["sample"]
+
+
+def test_traffic_summary_lookup(tmp_path, monkeypatch):
+    f = tmp_path / "traffic.txt"
+    f.write_text("# comment\nworkload = h3_video_l37810\n"
+                 f"attn_hip_sha256_16 = {bench.kernel_source_hash()}\nhbm_bytes_per_launch = 123456\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.measured_traffic("h3_video_l37810") == 123456.0
+    assert bench.measured_traffic("dense_h8_l4096") is None  # another workload
+    f.write_text("workload = h3_video_l37810\nattn_hip_sha256_16 = 0000\nhbm_bytes_per_launch = 1\n")
+    assert bench.measured_traffic("h3_video_l37810") is None  # taken from another kernel source
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert p.returncode == 2 and "one GPU" in p.stderr
