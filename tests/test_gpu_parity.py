@@ -316,6 +316,30 @@ def test_queries_without_keys_give_zeros():
     assert np.all(ref[0:5] == 0) and np.all(ref[10:] == 0)
 
 
+@pytest.mark.timeout(600)
+def test_long_key_sequence_reads_scales_through_the_scalar_cache():
+    """More than 2048 key blocks per segment: the kernel reads the K block scales through
+    the scalar cache instead of copying them to LDS.  Output vs the oracle; the fused-Q
+    forward on the same inputs is bit-identical."""
+    _need_gpu()
+    g = torch.Generator().manual_seed(77)
+    H, Lq, Lk = 2, 200, 2048 * 64 + 1000
+    q = torch.randn((1, Lq, H, 128), generator=g).to(torch.bfloat16)
+    k = (torch.randn((1, Lk, H, 128), generator=g) + 1.5).to(torch.bfloat16)
+    v = torch.randn((1, Lk, H, 128), generator=g).to(torch.bfloat16)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    quant = B.sattn_quantize_qkv(qd, kd, vd)
+    out = B.sattn_fwd(quant, 1, H, Lq, Lk, 0.0884)
+    kv = B.sattn_quantize_kv(qd, kd, vd)
+    fused = B.sattn_fwd_fused(kv, qd, 0.0884, Lk=Lk)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, out)
+    _say("[oracle] long key sequence: 200 rows x 132,072 keys x 2 heads")
+    oq = O.quantize(W.packed_float64(q), W.packed_float64(k), W.packed_float64(v), [0, Lq], [0, Lk])
+    ref = O.attention(oq, 0.0884)
+    _check_output(out[0].float().cpu().numpy().astype(np.float64), ref, "Lk=132072")
+
+
 @pytest.mark.timeout(900)
 def test_large_shape_sampled_heads():
     """The 74K-token, 56-head shape in the bench's launch configuration: every quantized byte
