@@ -272,7 +272,7 @@ __device__ __forceinline__ float softmax_pv(Pipe& c, v16i (&acc)[2], float sig, 
       float arg = __builtin_fmaf(__int_as_float(acc[t][4 * q4 + r3]) - kAccBiasF, sig, -mm);
       if (TAIL && 32 * t + 8 * q4 + 4 * g + r3 >= kvalid) arg = -INFINITY;
       pv[r3] = __builtin_amdgcn_exp2f(arg);  // 448 * P
-      ps[r3] += pv[r3];
+      ps[r3] = j == 0 ? pv[r3] : ps[r3] + pv[r3];
     }
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Wuninitialized"
@@ -281,6 +281,9 @@ __device__ __forceinline__ float softmax_pv(Pipe& c, v16i (&acc)[2], float sig, 
 #pragma clang diagnostic pop
     w01 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], w01, true);
     pb[j] = w01;
+    // keep the row-sum adds in their group, between the exponentials (left to itself the
+    // compiler sinks all 32 to the end of the step, where they issue back to back)
+    asm volatile("" : "+v"(ps[0]), "+v"(ps[1]), "+v"(ps[2]), "+v"(ps[3]));
   }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (NEXT) {
