@@ -314,6 +314,10 @@ def test_queries_without_keys_give_zeros():
     ref = O.attention(oq, 0.1)
     _check_output(out[5:10].astype(np.float64), ref[5:10], "seg 1")
     assert np.all(ref[0:5] == 0) and np.all(ref[10:] == 0)
+    # the fused-Q forward on the same packed batch (empty key segments included)
+    kv = B.sattn_quantize_kv(q.cuda(), k.cuda(), v.cuda(), cq, ck)
+    fused = B.sattn_fwd_fused(kv, q.cuda(), 0.1, cq, ck, Lk=7).float().cpu().numpy()
+    assert np.array_equal(fused, out)
 
 
 @pytest.mark.timeout(600)
