@@ -95,6 +95,21 @@ def cpu_baseline(w, inp, att_heads=8, rows=1024):
     }
 
 
+def _pct(xs, p):
+    """p-th percentile (linear interpolation) of a list."""
+    xs = sorted(xs)
+    r = (len(xs) - 1) * p / 100.0
+    lo = int(r)
+    hi = min(lo + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (r - lo)
+
+
+def _cv(xs):
+    """Coefficient of variation (standard deviation over mean)."""
+    m = sum(xs) / len(xs)
+    return (sum((x - m) ** 2 for x in xs) / len(xs)) ** 0.5 / m if m else 0.0
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -214,6 +229,11 @@ def main():
         "breakdown": {
             "fwd_ms_avg": fwd_avg,
             "fwd_ms_min": min(fwd_ms),
+            "fwd_ms_p10": _pct(fwd_ms, 10),
+            "fwd_ms_p50": _pct(fwd_ms, 50),
+            "fwd_ms_p90": _pct(fwd_ms, 90),
+            "fwd_cv": _cv(fwd_ms),
+            "samples": len(fwd_ms),
             "quant_ms_avg": quant_avg,
             "fwd_tops": achieved,
             "quant_gbs": quant_bytes / (quant_avg * 1e-3) / 1e9,

@@ -32,3 +32,10 @@ def test_more_than_one_gpu_is_refused():
     p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert p.returncode == 2 and "one GPU" in p.stderr
+
+
+def test_percentiles_and_cv():
+    xs = [4.0, 1.0, 3.0, 2.0, 5.0]
+    assert bench._pct(xs, 0) == 1.0 and bench._pct(xs, 50) == 3.0 and bench._pct(xs, 100) == 5.0
+    assert bench._pct(xs, 10) == 1.4
+    assert abs(bench._cv([2.0, 4.0]) - 1.0 / 3.0) < 1e-12
