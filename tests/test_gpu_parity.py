@@ -273,7 +273,8 @@ def test_repeated_launches_are_bitwise_identical():
         assert torch.equal(o2, out)
 
 
-@pytest.mark.parametrize("Lq,Lk", [(1, 1), (5, 64), (64, 65), (300, 3), (257, 1000)])
+@pytest.mark.parametrize("Lq,Lk", [(1, 1), (5, 64), (64, 65), (300, 3), (257, 1000), (31, 129), (33, 63), (127, 191),
+                                   (128, 128), (129, 576), (200, 897), (96, 1280)])
 def test_small_shapes_and_untouched_padding(Lq, Lk):
     _need_gpu()
     g = torch.Generator().manual_seed(Lq * 1000 + Lk)
