@@ -273,6 +273,18 @@ def test_repeated_launches_are_bitwise_identical():
         assert torch.equal(o2, out)
 
 
+def test_thousand_launches_of_the_fixed_shape_agree():
+    """The pages' fixed shape (B=1, H=1, 128 queries, 192 keys in three K64 epochs) run
+    1,000 times back to back on one stream: every output identical to the first."""
+    c = case("fixed_q128_kv192")
+    w = c["w"]
+    outs = torch.empty((1000, 1, 128, 1, 128), dtype=torch.bfloat16, device="cuda")
+    for i in range(1000):
+        B.sattn_fwd(c["quant"], 1, 1, 128, 192, w.sm_scale, out=outs[i])
+    torch.cuda.synchronize()
+    assert torch.equal(outs, c["out"].expand_as(outs))
+
+
 @pytest.mark.parametrize("Lq,Lk", [(1, 1), (5, 64), (64, 65), (300, 3), (257, 1000), (31, 129), (33, 63), (127, 191),
                                    (128, 128), (129, 576), (200, 897), (96, 1280)])
 def test_small_shapes_and_untouched_padding(Lq, Lk):
