@@ -12,8 +12,9 @@
 //  * One workgroup = 4 waves = 128 queries of one (segment, head); two workgroups share a
 //    CU, so each SIMD runs two waves of up to 256 VGPRs.  Each wave owns 32 queries end to
 //    end: Q operand, scores, running max and denominator, and the FP32 O accumulators.
-//    The softmax's vector work (about five VALU instructions per score, two of them
-//    transcendental-rate) is the binding resource; the MFMA work runs beside it.
+//    The softmax's vector work (about five VALU instructions per score: a subtraction,
+//    an FMA, an exponential, an add, half an FP8 pack and half a three-input max) is the
+//    binding resource; the MFMA work runs beside it.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_i32_32x32x32_i8: each lane
 //    owns one query column and 32 of the epoch's 64 keys, so the row max and row sum are
 //    in-lane plus one v_permlane32_swap between the two half-waves.
@@ -29,11 +30,14 @@
 //    quantizer with its keys permuted to match, so no probability goes through LDS.
 //  * K and V tiles (8 KiB each per epoch) stream into three-slot LDS rings with
 //    global_load_lds_dwordx4 (no VGPR staging), two epochs ahead of their use; one
-//    barrier per epoch.  Between the
-//    exponentials of epoch e the wave issues the P.V MFMAs of epoch e-1 and, as each
-//    score tile of epoch e is consumed, the QK MFMAs of epoch e+1 into the same
-//    registers: no MFMA result is waited for inside a step, and matrix cores and vector
-//    ALUs work at the same time.
+//    barrier per epoch.  The softmax of epoch e runs in eight groups of four
+//    probabilities, each led by one MFMA: the P.V MFMAs of epoch e-1, then, once a score
+//    tile of epoch e is consumed, the QK MFMAs of epoch e+1 into the same registers.  No
+//    MFMA result is waited for inside a step, and matrix cores and vector ALUs work at
+//    the same time.
+//  * The segment's K block scales are copied to LDS once (no scalar load in flight during
+//    a step).  With sattn_fwd_fused the workgroup also quantizes its own queries from the
+//    BF16 view in the prologue, with the quantizer's arithmetic.
 //  * The O rescale by alpha is skipped when no row of the wave changed its max (alpha is
 //    then exactly 1, so skipping is bit-identical).
 //  * Work items (segment, head, 128-query tile) are ordered so that consecutive
