@@ -273,6 +273,31 @@ def test_repeated_launches_are_bitwise_identical():
         assert torch.equal(o2, out)
 
 
+def test_many_tiny_segments_beyond_the_sorted_schedule():
+    """5,000 packed segments of 0..6 queries and 0..9 keys: more segments than the
+    longest-first schedule sorts (4,096), so the launch keeps the input order."""
+    _need_gpu()
+    rng = np.random.default_rng(5)
+    lq, lk = rng.integers(0, 7, 5000), rng.integers(0, 10, 5000)
+    cu_q, cu_k = [0] + [int(x) for x in np.cumsum(lq)], [0] + [int(x) for x in np.cumsum(lk)]
+    g = torch.Generator().manual_seed(5)
+    H = 2
+    q = torch.randn((cu_q[-1], H, 128), generator=g).to(torch.bfloat16)
+    k = torch.randn((cu_k[-1], H, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((cu_k[-1], H, 128), generator=g).to(torch.bfloat16)
+    cq, ck = _tensor_cu(cu_q), _tensor_cu(cu_k)
+    quant = B.sattn_quantize_qkv(q.cuda(), k.cuda(), v.cuda(), cq, ck)
+    out = B.sattn_fwd_varlen(quant, cq, ck, cu_q[-1], 0.1)
+    torch.cuda.synchronize()
+    oq = O.quantize(W.packed_float64(q), W.packed_float64(k), W.packed_float64(v), cu_q, cu_k)
+    ref = O.attention(oq, 0.1)
+    got = out.float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    assert np.max(err) <= MAX_REL * np.max(np.abs(ref)) and np.mean(err) <= MAE
+    empty_k = np.repeat(lk == 0, lq)
+    assert np.all(got[empty_k] == 0)
+
+
 def test_thousand_launches_of_the_fixed_shape_agree():
     """The pages' fixed shape (B=1, H=1, 128 queries, 192 keys in three K64 epochs) run
     1,000 times back to back on one stream: every output identical to the first."""
