@@ -56,7 +56,6 @@ namespace sattn {
 
 constexpr int kWaves = 4;                  // waves per workgroup: two workgroups per CU
 constexpr int kLoaderWaves = 4;            // waves that stream the K/V tiles
-constexpr bool kQInLds = kWaves > 4;       // Q operand in LDS (frees 16 VGPRs) or in registers
 constexpr int kWavesPerSimd = kWaves > 4 ? kWaves / 4 : 2;
 constexpr int kQPerWG = kWaves * 32;       // queries per workgroup
 constexpr int kQBlocksPerWG = kWaves / 2;  // 64-query blocks per workgroup
@@ -109,7 +108,6 @@ __shared__ __attribute__((aligned(16))) uint8_t g_k2[kTileBytes];
 __shared__ __attribute__((aligned(16))) uint8_t g_v0[kTileBytes];
 __shared__ __attribute__((aligned(16))) uint8_t g_v1[kTileBytes];
 __shared__ __attribute__((aligned(16))) uint8_t g_v2[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_qop[kQInLds ? kWaves : 1][kQInLds ? 4096 : 16];  // Q operands
 // K block scales of the workgroup's segment, copied to LDS at the start (segments of at
 // most kKsLds key blocks; longer ones read them through the scalar cache).  A scalar load
 // in flight would make every LDS wait of the step a full lgkmcnt(0) wait: SMEM results
@@ -159,7 +157,6 @@ struct Pipe {
   v16f oacc[4];  // O^T, 32 channels x 32 queries per tile
   v4i qop[4];            // this wave's Q operand (register copy)
   v16i bias;             // kAccBias in every element: the start value of the QK accumulators
-  const uint8_t* qlds;   // this wave's Q operand in LDS
   v8i pb[2];     // E4M3 probabilities of even / odd epochs (PV deferred one step)
   float alpha_prev;  // its rescale factor, applied to O just before its PV is accumulated
   float m, dpart, sig_q;
@@ -188,27 +185,13 @@ __device__ __forceinline__ void issue_tile(const Pipe& c, const uint8_t* src_til
   for (int j = 0; j < kChunksPerTile; ++j) dma_chunk(tile, c.loff[j], slot + (j * kLoaderWaves + c.wave) * 1024);
 }
 
-// One S^T tile t: acc_t = K(keys 32t..32t+31) . Q^T over 128 channels, with the K operands
-// already in registers.  The wave's Q operand is either in registers (qop) or in LDS at
-// Ql (four 1 KiB lane-ordered chunks).
-__device__ __forceinline__ void qk_mfma(v16i& acc_t, const v4i (&ka)[4], const v4i (&qop)[4], const uint8_t* Ql,
-                                        int lane) {
+// One S^T tile t of the first epoch: acc_t = K(keys 32t..32t+31) . Q^T over 128 channels,
+// started at kAccBias (later epochs run these MFMAs inside the softmax of the step before).
+__device__ __forceinline__ void qk_tile(v16i& acc_t, const uint8_t* Kl, const v4i (&qop)[4], int lane, int t) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc_t[i] = kAccBias;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    v4i b;
-    if constexpr (kQInLds) b = *reinterpret_cast<const v4i*>(Ql + (u * 64 + lane) * 16);
-    else b = qop[u];
-    acc_t = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[u], b, acc_t, 0, 0, 0);
-  }
-}
-__device__ __forceinline__ void qk_tile(v16i& acc_t, const uint8_t* Kl, const v4i (&qop)[4], const uint8_t* Ql,
-                                        int lane, int t) {
-  v4i ka[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) ka[u] = load_k(Kl, lane, t, u);
-  qk_mfma(acc_t, ka, qop, Ql, lane);
+  for (int u = 0; u < 4; ++u) acc_t = __builtin_amdgcn_mfma_i32_32x32x32_i8(load_k(Kl, lane, t, u), qop[u], acc_t, 0, 0, 0);
 }
 
 // Online softmax of epoch e for this lane's query (32 of the 64 keys; the other 32 are in
@@ -449,7 +432,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     for (int i = 0; i < 16; ++i) c.oacc[w][i] = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) c.pb[0][i] = c.pb[1][i] = 0;
-  c.qlds = g_qop[kQInLds ? wave : 0];
 #pragma unroll
   for (int u = 0; u < 4; ++u) c.qop[u] = v4i{0, 0, 0, 0};
   // Fused Q preparation (sattn_fwd_fused): lane g*32 + i holds token 32*hq + i of the
@@ -480,10 +462,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int8_t* src = qt_ptr + ((hq * 4 + u) * 64 + lane) * 16;
-      if constexpr (kQInLds)  // streamed into LDS; landed by the first barrier
-        __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(g_qop[wave] + u * 1024), 16, 0, 0);
-      else
-        c.qop[u] = *reinterpret_cast<const v4i*>(src);
+      c.qop[u] = *reinterpret_cast<const v4i*>(src);
     }
     // Retire the Q loads here, with a wait the compiler sees: otherwise its wait-count
     // bookkeeping keeps them pending into the epoch loop and waits on vmcnt before the QK
@@ -548,8 +527,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     c.sig_q = scale * p.c32;
   }
   if (nkb > 0) {
-    qk_tile(acc[0], kslot<0>(), c.qop, c.qlds, lane, 0);
-    qk_tile(acc[1], kslot<0>(), c.qop, c.qlds, lane, 1);
+    qk_tile(acc[0], kslot<0>(), c.qop, lane, 0);
+    qk_tile(acc[1], kslot<0>(), c.qop, lane, 1);
   }
   const int nfull = nkb - 1;  // epochs before the last one
   int e = 0;
