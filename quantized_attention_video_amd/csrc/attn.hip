@@ -295,12 +295,13 @@ __device__ __forceinline__ void rescale(Pipe& c) {
   }
 }
 
-// Pipeline step for epoch e (ST = e % kUnroll).  STEADY steps have e + 3 < nkb: every
-// tile request and scale load is in range, so they run without tests or branches.  Its scores are already in acc (QK issued
+// Pipeline step for epoch e (ST = e % kUnroll).  Its scores are already in acc (QK issued
 // during the previous step).  Wait until K(e+1) and V(e-1) have landed (the requests of
-// step e-1 may stay in flight), barrier, request K(e+3) and V(e+1), then
-// rescale O by alpha(e-1) and run the softmax of e with PV(e-1) and QK(e+1) interleaved.
-// LAST marks the final epoch (TAIL masks its keys), which also accumulates its own PV.
+// step e-1 may stay in flight), barrier, request K(e+3) and V(e+1), then rescale O by
+// alpha(e-1) and run the softmax of e with PV(e-1) and QK(e+1) interleaved.  LAST marks
+// the final epoch (TAIL masks its keys), which also accumulates its own PV.  STEADY steps
+// have e + 3 < nkb: every tile request and scale load is in range, so they run without
+// tests or branches.
 template <int ST, bool LAST, bool TAIL, bool DUMP, bool KSL, bool STEADY = false>
 __device__ __forceinline__ void pipe_step(Pipe& c, int e, int kvalid, const Dump& dump, v16i (&acc)[2]) {
   constexpr int KS = ST % kRing, KN = (ST + 1) % kRing, VP = (ST + 2) % kRing;
