@@ -298,6 +298,34 @@ def test_many_tiny_segments_beyond_the_sorted_schedule():
     assert np.all(got[empty_k] == 0)
 
 
+def test_degenerate_values():
+    """Zero scales everywhere they can occur: segment 0 has K constant over its tokens (the
+    smoothed K is zero, every k_scale 0, every score 0: uniform attention); segment 1 has an
+    all-zero 64-query block (q_scale 0) and an all-zero V channel (v_scale 0)."""
+    _need_gpu()
+    g = torch.Generator().manual_seed(11)
+    H, L = 2, 300
+    q = torch.randn((2, L, H, 128), generator=g)
+    k = torch.randn((2, L, H, 128), generator=g)
+    v = torch.randn((2, L, H, 128), generator=g)
+    k[0] = torch.randn((1, H, 128), generator=g)  # constant over segment 0's tokens
+    q[1, 64:128] = 0.0
+    v[1, :, :, 5] = 0.0
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    quant = B.sattn_quantize_qkv(q.cuda(), k.cuda(), v.cuda())
+    out = B.sattn_fwd(quant, 2, H, L, L, 0.0884)
+    torch.cuda.synchronize()
+    assert not quant.k_scale[:, :5].any()  # segment 0's five K blocks
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.all(got[1, :, :, 5] == 0)
+    oq = O.quantize(W.packed_float64(q), W.packed_float64(k), W.packed_float64(v), [0, L, 2 * L], [0, L, 2 * L])
+    ref = O.attention(oq, 0.0884)
+    for si in range(2):
+        _check_output(got[si], ref[si * L:(si + 1) * L], f"degenerate seg {si}")
+    # uniform attention: every query of segment 0 sees the same weights, so all its rows agree
+    assert np.all(got[0] == got[0, :1])
+
+
 def test_thousand_launches_of_the_fixed_shape_agree():
     """The pages' fixed shape (B=1, H=1, 128 queries, 192 keys in three K64 epochs) run
     1,000 times back to back on one stream: every output identical to the first."""
