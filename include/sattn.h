@@ -151,7 +151,8 @@ SATTN_API sattn_status sattn_quant_query(int nseg, int64_t total_q, int64_t tota
  *
  * `workspace` must hold quant_workspace_bytes from sattn_quant_query (16-byte aligned);
  * it is scratch: its contents are undefined after the call.  Returns SATTN_ENOSPACE when
- * a capacity in `out` or workspace_bytes is too small.
+ * a capacity in `out` or workspace_bytes is too small, and SATTN_EUNSUPPORTED when the
+ * statistics and Q blocks together exceed 2^32 - 1 workgroups (far beyond any memory).
  *
  * K and V only: with out->q and out->q_scale both NULL, the Q step is skipped and the q
  * view is not read (it may be NULL); this is the preparation sattn_fwd_fused needs.

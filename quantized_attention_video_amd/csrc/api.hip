@@ -131,6 +131,8 @@ sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in 
   a.ws_sums_bytes = ws.sums;
   a.ws_vmax_bytes = ws.vmax;
   if (a.q_blocks > 0x7fffffff || a.k_blocks > 0x7fffffff) return SATTN_EUNSUPPORTED;
+  // the statistics and the Q blocks share one 1-D grid
+  if ((int64_t)stats_chunks(nseg, H) * nseg * H + a.q_blocks * H > 0xffffffffLL) return SATTN_EUNSUPPORTED;
   return launch_quantize(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SATTN_OK : SATTN_EHIP;
 }
 
