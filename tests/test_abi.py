@@ -101,6 +101,9 @@ def test_quantize_validation():
     assert call(wsb=16) == B.SATTN_ENOSPACE
     for rows in (1, 16, 48, 128, -32):
         assert call(out=_quant_struct(rows=rows)) == B.SATTN_EINVAL
+    # statistics blocks (one per segment-head here) plus Q blocks beyond a 1-D grid of 2^32 - 1
+    big = dict(nseg=65535, H=65535, Lq=1, Lk=1, out=_quant_struct(cap=1 << 40), wsb=1 << 62)
+    assert call(**big) == B.SATTN_EUNSUPPORTED
 
 
 def test_fwd_validation():
