@@ -38,8 +38,9 @@
 //  * The segment's K block scales are copied to LDS once (no scalar load in flight during
 //    a step).  With sattn_fwd_fused the workgroup also quantizes its own queries from the
 //    BF16 view in the prologue, with the quantizer's arithmetic.
-//  * The O rescale by alpha is skipped when no row of the wave changed its max (alpha is
-//    then exactly 1, so skipping is bit-identical).
+//  * The O rescale by alpha runs only in the lanes whose row max changed, and not at all
+//    when no row of the wave changed (alpha is then exactly 1, so skipping is
+//    bit-identical).
 //  * Work items (segment, head, 128-query tile) are ordered so that consecutive
 //    workgroups dispatched to one XCD (workgroup b runs on XCD b mod 8) take the same
 //    head and neighbouring query tiles, so the CUs of an XCD stream the same K/V tiles
@@ -283,11 +284,13 @@ __device__ __forceinline__ float softmax_pv(Pipe& c, v16i (&acc)[2], float sig, 
   return alpha;
 }
 
-// O *= alpha of the epoch whose PV is about to be accumulated (skipped when no row of the
-// wave changed its max: alpha is then exactly 1).
+// O *= alpha of the epoch whose PV is about to be accumulated, only in the lanes (query
+// rows) whose max changed: elsewhere alpha is exactly 1.  The whole block is skipped when
+// no row of the wave changed; masked lanes cost the same issue slots but no ALU switching,
+// which counts on a power-capped part.
 __device__ __forceinline__ void rescale(Pipe& c) {
   const float a = c.alpha_prev;
-  if (__any(a != 1.0f)) {
+  if (a != 1.0f) {
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
