@@ -1,6 +1,7 @@
 """Throughput of the quantized attention hot path on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--fused-q]
+                [--latency [--samples S]]
 
 A step is one pass of the whole path over one batch of synthetic input already resident
 in HBM: sattn_quantize_qkv (K statistics, INT8 Q/K tiles, E4M3 V tiles) followed by
@@ -11,6 +12,13 @@ B=1, H=32, L=37,810 packed tokens, D=128, Q/K/V projection-strided slices of one
 runs on; its algorithmic operation count over that time, against the 5.0 POP/s dense
 INT8/FP8 MFMA peak, is the roofline entry.  The CPU baseline times the FP64 oracle on a
 bounded sample of the same workload and extrapolates linearly.
+
+--latency (for the small shapes, e.g. --workload fixed_q128_kv192) reports the per-launch
+time of sattn_fwd the way the pages time their fixed-shape kernel: samples of 20
+back-to-back launches, the per-launch time being a sample's event interval over 20; the
+launches are replayed from a captured HIP graph so that host enqueue time (Python and
+ctypes) does not stretch the interval, with the eager figure beside it.  Its CPU baseline
+is the whole oracle on the whole shape, on one host thread and on all of them.
 
 --fused-q times the other form of the same path: sattn_quantize_qkv for K and V only, then
 sattn_fwd_fused, which quantizes Q inside the attention launch from the BF16 view (the
@@ -120,6 +128,124 @@ def _cpu_model():
     return "unknown"
 
 
+# The pages' fixed-shape figure (B=1, H=1, Q=128, KV=192): VEA-B per-launch p50 over 500
+# samples of 20 launches on GB10 ([Report] "Timing"); context for --latency, another chip.
+PAGES_FIXED_SHAPE_US = 14.426
+
+
+def cpu_oracle_full(w, inp):
+    """The whole oracle (quantization + attention of every row and head) on the whole
+    shape, timed on one host thread and on all of them (BLAS threads)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import sattn as O
+    from quantized_attention_video_amd import workloads as W
+
+    q, k, v = (W.packed_float64(inp[n]) for n in "qkv")
+
+    def run():
+        t0 = time.perf_counter()
+        O.attention(O.quantize(q, k, v, inp["cu_q"], inp["cu_k"]), w.sm_scale)
+        return time.perf_counter() - t0
+
+    run()  # warm-up (imports, first-touch)
+    t_all = min(run() for _ in range(3))
+    with threadpool_limits(limits=1):
+        t_one = min(run() for _ in range(3))
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": t_all * 1e6, "unit": "us", "cores": threads, "kind": "oracle",
+            "single_thread_us": t_one * 1e6,
+            "sample": "FP64 oracle, whole shape (quantize + attention), best of 3", "cpu": _cpu_model()}
+
+
+def latency(args, w, torch, B):
+    """Per-launch time of sattn_fwd on one dense shape (see the module docstring)."""
+    from quantized_attention_video_amd import workloads as W
+
+    inp = W.make_inputs(w)
+    dev = W.to_device(inp)
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    Bn, Lq, H = q.shape[:3]
+    Lk = k.shape[1]
+    quant = B.alloc_quantized(Bn, Bn * Lq, Bn * Lk, H)
+    out = torch.empty((Bn, Lq, H, 128), dtype=torch.bfloat16, device="cuda")
+    B.sattn_quantize_qkv(q, k, v, out=quant)
+    per = 20
+
+    def fwd():
+        B.sattn_fwd(quant, Bn, H, Lq, Lk, w.sm_scale, out=out)
+
+    fwd()
+    torch.cuda.synchronize()
+    ref = out.clone()
+
+    def sample_times(launch, n, count):
+        """n event intervals around `launch()`, each covering `count` kernel launches (us per launch)."""
+        for _ in range(args.warmup):
+            launch()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        stream = torch.cuda.current_stream()
+        for a, b in ev:
+            a.record(stream)
+            launch()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 / count for a, b in ev]
+
+    def eager20():
+        for _ in range(per):
+            fwd()
+
+    eager = sample_times(eager20, args.samples, per)
+    single = sample_times(fwd, 4 * args.samples, 1)
+    # the same 20 launches captured once and replayed (no host work between kernels)
+    g = torch.cuda.CUDAGraph()
+    out.zero_()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        eager20()
+    graph = sample_times(g.replay, args.samples, per)
+    replays_ok = True
+    for _ in range(3):  # every replay, with eager work between, must reproduce the eager output
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        replays_ok &= bool(torch.equal(out, ref))
+        fwd()
+        torch.cuda.synchronize()
+
+    def stats(xs):
+        return {"p10": _pct(xs, 10), "p50": _pct(xs, 50), "p90": _pct(xs, 90), "cv": _cv(xs), "samples": len(xs)}
+
+    value = _pct(graph, 50)
+    line = {
+        "metric": "sattn_fwd time per launch (20 back-to-back launches per sample)",
+        "value": value,
+        "unit": "us",
+        "n_gpus": 1,
+        "higher_is_better": False,
+        "vs_baseline": value / PAGES_FIXED_SHAPE_US if w.name == "fixed_q128_kv192" else None,
+        "dtype": "int8 (QK) + fp8 e4m3 (PV), fp32 softmax",
+        "data": f"synthetic (seeded BF16; {w.notes})",
+        "config": {"workload": w.name, "B": Bn, "H": H, "Lq": Lq, "Lk": Lk, "D": 128, "layout": w.layout,
+                   "launches_per_sample": per},
+        "graph_replay_us": stats(graph),
+        "eager_us": stats(eager),
+        "single_launch_us": stats(single),
+        "graph_replays_match_eager": replays_ok,
+        "tops_at_p50": w.ops() / (value * 1e-6) / 1e12,
+    }
+    if w.name == "fixed_q128_kv192":
+        line["context"] = (f"pages, GB10: {PAGES_FIXED_SHAPE_US} us per launch p50 (same shape, 500 x 20 "
+                           f"launches); vs_baseline = value / that")
+    if not args.no_cpu_baseline and w.ops() <= 1e9:  # larger shapes: the throughput mode's sampled baseline
+        line["cpu_baseline"] = cpu_oracle_full(w, inp)
+    print(json.dumps(line))
+    if not replays_ok:
+        raise SystemExit("graph replays differ from the eager output")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +255,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused-q", action="store_true",
                     help="step = K/V-only quantization + sattn_fwd_fused (Q prepared in the attention launch)")
+    ap.add_argument("--latency", action="store_true",
+                    help="per-launch time of sattn_fwd on a small dense shape (samples of 20 launches)")
+    ap.add_argument("--samples", type=int, default=500, help="--latency: samples of 20 launches")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run N plain 1 GiB device copies (counter calibration) and exit")
     args = ap.parse_args()
@@ -154,6 +283,9 @@ def main():
     w = W.get(args.workload)
     if w.varlen:
         raise SystemExit("bench.py times dense workloads; the packed one is covered by the GPU tests")
+    if args.latency:
+        latency(args, w, torch, B)
+        return
     inp = W.make_inputs(w)
     dev = W.to_device(inp)
     q, k, v = dev["q"], dev["k"], dev["v"]

@@ -1,4 +1,4 @@
-"""Host-side pieces of bench.py (no GPU): the CPU baseline on a small workload, the
+"""Host-side pieces of bench.py (no GPU): the CPU baselines on a small workload, the
 traffic-summary lookup, and the refusal of more than one GPU."""
 import os
 import subprocess
@@ -15,6 +15,13 @@ def test_cpu_baseline_small_sample():
     r = bench.cpu_baseline(w, W.make_inputs(w), att_heads=1, rows=64)
     assert r["kind"] == "oracle" and r["unit"] == "TOPS" and r["value"] > 0 and r["cores"] >= 1
     assert "extrapolated" in r["sample"]
+
+
+def test_cpu_oracle_full_small_shape():
+    w = W.get("fixed_q128_kv192")
+    r = bench.cpu_oracle_full(w, W.make_inputs(w))
+    assert r["kind"] == "oracle" and r["unit"] == "us" and r["value"] > 0 and r["single_thread_us"] > 0
+    assert r["cores"] >= 1
 
 
 def test_traffic_summary_lookup(tmp_path, monkeypatch):
