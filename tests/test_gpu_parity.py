@@ -80,20 +80,18 @@ NAMES = ["fixed_q128_kv192", "dense_h8_l4096", "ragged_b2_h16_l1000", "ragged_b2
          "h3_video_l37810"]
 
 
-@pytest.mark.parametrize("name", NAMES)
-def test_quantized_buffers_bit_exact(name):
-    c = case(name)
-    w, quant, oq, inp = c["w"], c["quant"], c["oq"], c["inp"]
+def _assert_quantized_equal(quant, oq, bq, bk, H):
+    """Every quantized byte and scale of every segment equals the oracle's (bq, bk: first
+    quantized block of each segment)."""
     qt, kt, vt = (getattr(quant, n).cpu().numpy() for n in ("q", "k", "v"))
     qs, ks = quant.q_scale.cpu().numpy(), quant.k_scale.cpu().numpy()
     km, vs = quant.k_mean.cpu().numpy(), quant.v_scale.cpu().numpy()
-    bq, bk = _blocks(inp["cu_q"], w), _blocks(inp["cu_k"], w)
     for si, seg in enumerate(oq):
         Lq, Lk = seg["q8"].shape[0], seg["k8"].shape[0]
         nq, nk = -(-Lq // 64), -(-Lk // 64)
         assert np.array_equal(km[si], seg["k_mean"].astype(np.float32)), f"k_mean seg {si}"
         assert np.array_equal(vs[si], seg["v_scale"].astype(np.float32)), f"v_scale seg {si}"
-        for h in range(w.H):
+        for h in range(H):
             gq = B.untile_qk(qt[h, bq[si]:bq[si] + nq])
             gk = B.untile_qk(kt[h, bk[si]:bk[si] + nk])
             gv = B.untile_v(vt[h, bk[si]:bk[si] + nk])
@@ -103,6 +101,13 @@ def test_quantized_buffers_bit_exact(name):
             assert not gq[Lq:].any() and not gk[Lk:].any() and not gv[Lk:].any(), "padding must be zero"
             assert np.array_equal(qs[h, bq[si]:bq[si] + nq], seg["q_scale"][h].astype(np.float32))
             assert np.array_equal(ks[h, bk[si]:bk[si] + nk], seg["k_scale"][h].astype(np.float32))
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_quantized_buffers_bit_exact(name):
+    c = case(name)
+    w, inp = c["w"], c["inp"]
+    _assert_quantized_equal(c["quant"], c["oq"], _blocks(inp["cu_q"], w), _blocks(inp["cu_k"], w), w.H)
 
 
 @pytest.mark.parametrize("name,seg,head", [("fixed_q128_kv192", 0, 0), ("dense_h8_l4096", 0, 5),
@@ -172,6 +177,13 @@ def test_q32_quantized_buffers_bit_exact(name):
             gk = B.untile_qk(kt[h, bk[si]:bk[si] + nk])
             assert np.array_equal(gk[:Lk], seg["k8"][:, h, :].astype(np.int8)), f"k8 seg {si} head {h}"
             assert np.array_equal(ks[h, bk[si]:bk[si] + nk], seg["k_scale"][h].astype(np.float32))
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_quantized_buffers_bit_exact(name):
+    c = case(name)
+    w, inp = c["w"], c["inp"]
+    _assert_quantized_equal(c["quant"], c["oq"], _blocks(inp["cu_q"], w), _blocks(inp["cu_k"], w), w.H)
 
 
 @pytest.mark.parametrize("name,seg,head", [("fixed_q128_kv192", 0, 0), ("ragged_b2_h16_l1000", 1, 9),
@@ -275,7 +287,8 @@ def test_repeated_launches_are_bitwise_identical():
 
 def test_many_tiny_segments_beyond_the_sorted_schedule():
     """5,000 packed segments of 0..6 queries and 0..9 keys: more segments than the
-    longest-first schedule sorts (4,096), so the launch keeps the input order."""
+    longest-first schedule sorts (4,096), so the launch keeps the input order; one
+    statistics block per segment-head.  Bytes and output against the oracle."""
     _need_gpu()
     rng = np.random.default_rng(5)
     lq, lk = rng.integers(0, 7, 5000), rng.integers(0, 10, 5000)
@@ -290,6 +303,9 @@ def test_many_tiny_segments_beyond_the_sorted_schedule():
     out = B.sattn_fwd_varlen(quant, cq, ck, cu_q[-1], 0.1)
     torch.cuda.synchronize()
     oq = O.quantize(W.packed_float64(q), W.packed_float64(k), W.packed_float64(v), cu_q, cu_k)
+    # a per-segment K mean enters the scores as a per-query constant, to which the softmax is
+    # blind: only the bytes show whether every segment's statistics are the right ones
+    _assert_quantized_equal(quant, oq, B.segment_blocks(cu_q, None), B.segment_blocks(cu_k, None), H)
     ref = O.attention(oq, 0.1)
     got = out.float().cpu().numpy().astype(np.float64)
     err = np.abs(got - ref)
