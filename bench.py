@@ -118,6 +118,24 @@ def _cv(xs):
     return (sum((x - m) ** 2 for x in xs) / len(xs)) ** 0.5 / m if m else 0.0
 
 
+def copy_gbs(torch, nbytes=1 << 30, reps=5):
+    """HBM rate of a plain device copy (bytes read + written per second, GB/s): what a
+    pure streaming kernel reaches on this part, beside the 8 TB/s nameplate."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    rate = 2 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    return rate
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -330,6 +348,7 @@ def main():
     # algorithmic HBM bytes of the quantization pass: Q read once (2D) and written as INT8
     # (D); K and V read twice each (statistics, then quantization: 8D) and written once (2D)
     quant_bytes = H * Bn * ((0 if args.fused_q else 3 * 128 * Lq) + 10 * 128 * Lk)
+    copy_rate = copy_gbs(torch)  # after the timed steps
     step_name = ("sattn_quantize_qkv (K, V) + sattn_fwd_fused" if args.fused_q
                  else "sattn_quantize_qkv + sattn_fwd")
     result = {
@@ -370,6 +389,8 @@ def main():
             "fwd_tops": achieved,
             "quant_gbs": quant_bytes / (quant_avg * 1e-3) / 1e9,
             "quant_hbm_frac": quant_bytes / (quant_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "copy_gbs": copy_rate,
+            "quant_vs_copy": quant_bytes / (quant_avg * 1e-3) / 1e9 / copy_rate,
         },
         "cpu_baseline": None,
     }
