@@ -3,6 +3,9 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--fused-q]
                 [--latency [--samples S]]
 
+--workload takes any workload of quantized_attention_video_amd/workloads.py; a packed one
+(varlen_h24_4seg) runs sattn_quantize_qkv with cu_seqlens and sattn_fwd_varlen.
+
 A step is one pass of the whole path over one batch of synthetic input already resident
 in HBM: sattn_quantize_qkv (K statistics, INT8 Q/K tiles, E4M3 V tiles) followed by
 sattn_fwd (the fused attention kernel).  The default workload is the H3-like video layer:
@@ -71,9 +74,9 @@ def _head_slice(seg, n):
 
 def cpu_baseline(w, inp, att_heads=8, rows=1024):
     """Time the oracle on a bounded sample of the step: the quantization of all heads over
-    all tokens, and attention for `rows` query rows (half from each end) of `att_heads`
-    heads against all keys; the attention time is extrapolated linearly to every row and
-    head."""
+    all tokens, and attention for `rows` query rows (half from each end) of the first
+    segment's first `att_heads` heads against all of its keys; the attention time is
+    extrapolated linearly, by operation count, to every row, head and segment."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -84,23 +87,35 @@ def cpu_baseline(w, inp, att_heads=8, rows=1024):
     t0 = time.perf_counter()
     quant = O.quantize(q, k, v, inp["cu_q"], inp["cu_k"])
     t1 = time.perf_counter()
-    L = w.Lq
-    sel = np.concatenate([np.arange(0, rows // 2), np.arange(L - rows // 2, L)])
+    L0, Lk0 = w.seqlens_q()[0], w.seqlens_k()[0]
+    rows = min(rows, L0)
+    att_heads = min(att_heads, w.H)
+    sel = np.concatenate([np.arange(0, rows // 2), np.arange(L0 - (rows - rows // 2), L0)])
     O.attention([_head_slice(seg, att_heads) for seg in quant], w.sm_scale, rows={0: sel})
     t2 = time.perf_counter()
-    est = (t1 - t0) + (t2 - t1) * (w.H / att_heads) * (L / rows)
+    est = (t1 - t0) + (t2 - t1) * w.ops() / (4 * 128 * att_heads * rows * Lk0)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {
         "value": w.ops() / est / 1e12,
         "unit": "TOPS",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"FP64 oracle: quantization of all {w.H} heads over all {L} tokens ({t1 - t0:.1f} s) + "
-                   f"attention for {rows} query rows of {att_heads}/{w.H} heads against all keys "
-                   f"({t2 - t1:.1f} s); attention extrapolated linearly to all rows and heads: "
-                   f"full step = {est:.0f} s"),
+        "sample": (f"FP64 oracle: quantization of all {w.H} heads over all tokens ({t1 - t0:.1f} s) + "
+                   f"attention for {rows} query rows of {att_heads}/{w.H} heads of the first "
+                   f"{'segment' if w.varlen else 'sequence'} against all its keys ({t2 - t1:.1f} s); "
+                   f"attention extrapolated linearly by operation count to all rows, heads and "
+                   f"sequences: full step = {est:.0f} s"),
         "cpu": _cpu_model(),
     }
+
+
+def _data_recipe(w):
+    parts = ["seeded N(0,1) BF16"]
+    if w.k_bias_std:
+        parts.append(f"per-channel K bias N(0,{w.k_bias_std:g})")
+    if w.q_boost_frac:
+        parts.append(f"{w.q_boost_frac:.0%} of Q rows x8")
+    return "synthetic (" + ", ".join(parts) + ")"
 
 
 def _pct(xs, p):
@@ -245,7 +260,7 @@ def latency(args, w, torch, B):
         "higher_is_better": False,
         "vs_baseline": value / PAGES_FIXED_SHAPE_US if w.name == "fixed_q128_kv192" else None,
         "dtype": "int8 (QK) + fp8 e4m3 (PV), fp32 softmax",
-        "data": f"synthetic (seeded BF16; {w.notes})",
+        "data": _data_recipe(w),
         "config": {"workload": w.name, "B": Bn, "H": H, "Lq": Lq, "Lk": Lk, "D": 128, "layout": w.layout,
                    "launches_per_sample": per},
         "graph_replay_us": stats(graph),
@@ -299,28 +314,42 @@ def main():
     from quantized_attention_video_amd import workloads as W
 
     w = W.get(args.workload)
-    if w.varlen:
-        raise SystemExit("bench.py times dense workloads; the packed one is covered by the GPU tests")
     if args.latency:
+        if w.varlen:
+            raise SystemExit("--latency times dense shapes")
         latency(args, w, torch, B)
         return
     inp = W.make_inputs(w)
     dev = W.to_device(inp)
     q, k, v = dev["q"], dev["k"], dev["v"]
-    Bn, Lq, H = q.shape[:3]
-    Lk = k.shape[1]
-    quant = B.alloc_quantized(Bn, Bn * Lq, Bn * Lk, H, with_q=not args.fused_q)
-    out = torch.empty((Bn, Lq, H, 128), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
+    if w.varlen:  # packed [T, H, D] with cu_seqlens (block-diagonal attention per segment)
+        T, H = q.shape[0], q.shape[1]
+        nseg = len(w.seqlens)
+        Bn, Lq, Lk = 1, T, T  # for the byte count below: one packed sequence of T tokens
+        cq = torch.tensor(inp["cu_q"], dtype=torch.int32, device="cuda")
+        ck = torch.tensor(inp["cu_k"], dtype=torch.int32, device="cuda")
+        quant = B.alloc_quantized(nseg, T, T, H, with_q=not args.fused_q)
+        out = torch.empty((T, H, 128), dtype=torch.bfloat16, device="cuda")
+        ws = B.fwd_workspace(nseg)
+    else:
+        Bn, Lq, H = q.shape[:3]
+        Lk = k.shape[1]
+        cq = ck = None
+        quant = B.alloc_quantized(Bn, Bn * Lq, Bn * Lk, H, with_q=not args.fused_q)
+        out = torch.empty((Bn, Lq, H, 128), dtype=torch.bfloat16, device="cuda")
 
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        B.sattn_quantize_qkv(q, k, v, out=quant, stream=stream)
+        B.sattn_quantize_qkv(q, k, v, cq, ck, out=quant, stream=stream)
         if ev:
             ev[1].record(stream)
         if args.fused_q:
-            B.sattn_fwd_fused(quant, q, w.sm_scale, Lk=Lk, out=out, stream=stream)
+            B.sattn_fwd_fused(quant, q, w.sm_scale, cq, ck, Lk=Lk, out=out, workspace=ws if w.varlen else None,
+                              stream=stream)
+        elif w.varlen:
+            B.sattn_fwd_varlen(quant, cq, ck, T, w.sm_scale, out=out, workspace=ws, stream=stream)
         else:
             B.sattn_fwd(quant, Bn, H, Lq, Lk, w.sm_scale, out=out, stream=stream)
         if ev:
@@ -350,9 +379,10 @@ def main():
     quant_bytes = H * Bn * ((0 if args.fused_q else 3 * 128 * Lq) + 10 * 128 * Lk)
     copy_rate = copy_gbs(torch)  # after the timed steps
     step_name = ("sattn_quantize_qkv (K, V) + sattn_fwd_fused" if args.fused_q
-                 else "sattn_quantize_qkv + sattn_fwd")
+                 else "sattn_quantize_qkv + sattn_fwd_varlen" if w.varlen else "sattn_quantize_qkv + sattn_fwd")
     result = {
-        "metric": "attention TOPS (4*Lq*Lkv*D*H/s) at L=37,810 D=128; % of MFMA peak",
+        "metric": ("attention TOPS (4*Lq*Lkv*D*H/s) at L=37,810 D=128; % of MFMA peak" if w.name == "h3_video_l37810"
+                   else "attention TOPS (4*Lq*Lkv*D*H/s, summed over segments); % of MFMA peak"),
         "value": ops / (ms_per_step * 1e-3) / 1e12,
         "unit": "TOPS",
         "n_gpus": 1,
@@ -363,9 +393,11 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8 (QK) + fp8 e4m3 (PV), fp32 softmax",
-        "data": "synthetic (seeded N(0,1) BF16, per-channel K bias N(0,2))",
-        "config": {"workload": w.name, "B": Bn, "H": H, "Lq": Lq, "Lk": Lk, "D": 128,
-                   "layout": w.layout, "step": step_name},
+        "data": _data_recipe(w),
+        "config": ({"workload": w.name, "H": H, "seqlens": list(w.seqlens), "D": 128, "layout": w.layout,
+                    "step": step_name} if w.varlen else
+                   {"workload": w.name, "B": Bn, "H": H, "Lq": Lq, "Lk": Lk, "D": 128,
+                    "layout": w.layout, "step": step_name}),
         "roofline": {
             "bound": "mfma",
             "kernel": "attn_fwd_kernel",

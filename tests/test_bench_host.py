@@ -17,6 +17,19 @@ def test_cpu_baseline_small_sample():
     assert "extrapolated" in r["sample"]
 
 
+def test_cpu_baseline_packed_and_batched():
+    """The sampled baseline extrapolates by operation count, so it also covers packed
+    segments and batches of several sequences."""
+    tiny = W.Workload("tiny_packed", 99, H=2, seqlens=[100, 37, 0, 5], layout="packed")
+    r = bench.cpu_baseline(tiny, W.make_inputs(tiny), att_heads=1, rows=16)
+    assert r["value"] > 0 and "segment" in r["sample"]
+    w = W.get("ragged_b2_h16_l1000")
+    small = W.Workload("tiny_batch", 98, H=2, B=2, Lq=70, Lk=90, layout="blhd")
+    r = bench.cpu_baseline(small, W.make_inputs(small), att_heads=1, rows=16)
+    assert r["value"] > 0 and "sequence" in r["sample"]
+    assert w.ops() == 4 * 2 * 1000 * 1000 * 128 * 16
+
+
 def test_cpu_oracle_full_small_shape():
     w = W.get("fixed_q128_kv192")
     r = bench.cpu_oracle_full(w, W.make_inputs(w))
