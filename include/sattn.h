@@ -77,7 +77,7 @@ extern "C" {
 typedef int32_t sattn_status;
 #define SATTN_OK 0
 #define SATTN_EINVAL 1       /* bad pointer, size, stride, alignment or segment count   */
-#define SATTN_EUNSUPPORTED 2 /* well-formed but outside what the kernels implement (D)  */
+#define SATTN_EUNSUPPORTED 2 /* well-formed but outside what the kernels implement (D, grid size) */
 #define SATTN_ENOSPACE 3     /* a capacity or workspace is smaller than required       */
 #define SATTN_EHIP 4         /* a HIP launch or runtime call failed                    */
 
@@ -151,8 +151,9 @@ SATTN_API sattn_status sattn_quant_query(int nseg, int64_t total_q, int64_t tota
  *
  * `workspace` must hold quant_workspace_bytes from sattn_quant_query (16-byte aligned);
  * it is scratch: its contents are undefined after the call.  Returns SATTN_ENOSPACE when
- * a capacity in `out` or workspace_bytes is too small, and SATTN_EUNSUPPORTED when the
- * statistics and Q blocks together exceed 2^32 - 1 workgroups (far beyond any memory).
+ * a capacity in `out` or workspace_bytes is too small, and SATTN_EUNSUPPORTED when a
+ * launch would exceed 2^24 - 1 workgroups of 256 threads (one dispatch counts work-items
+ * in 32 bits; the statistics and Q blocks share one grid; far beyond what fits in memory).
  *
  * K and V only: with out->q and out->q_scale both NULL, the Q step is skipped and the q
  * view is not read (it may be NULL); this is the preparation sattn_fwd_fused needs.

@@ -52,6 +52,9 @@ int q_scale_shift(const sattn_qkv_quant* b) { return b->q_scale_rows == 32 ? 1 :
 
 int64_t ceil64(int64_t n) { return (n + 63) / 64; }
 
+// Largest grid of 256-thread workgroups one dispatch takes (it counts work-items in 32 bits).
+constexpr int64_t kMaxGroups256 = 0xffffffffLL / 256;
+
 // Largest token count whose blocks fit a capacity (cap = floor(T/64) + nseg).
 int64_t clip_for_cap(int64_t cap, int nseg) { return cap >= nseg ? (cap - nseg) * 64 + 63 : 0; }
 
@@ -130,9 +133,10 @@ sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in 
   a.workspace = workspace;
   a.ws_sums_bytes = ws.sums;
   a.ws_vmax_bytes = ws.vmax;
-  if (a.q_blocks > 0x7fffffff || a.k_blocks > 0x7fffffff) return SATTN_EUNSUPPORTED;
-  // the statistics and the Q blocks share one 1-D grid
-  if ((int64_t)stats_chunks(nseg, H) * nseg * H + a.q_blocks * H > 0xffffffffLL) return SATTN_EUNSUPPORTED;
+  // the statistics and the Q blocks share one 1-D grid; K/V blocks are the x extent of another
+  if (a.q_blocks > kMaxGroups256 || a.k_blocks > kMaxGroups256 ||
+      (int64_t)stats_chunks(nseg, H) * nseg * H + a.q_blocks * H > kMaxGroups256)
+    return SATTN_EUNSUPPORTED;
   return launch_quantize(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SATTN_OK : SATTN_EHIP;
 }
 
@@ -174,7 +178,7 @@ static sattn_status fwd_dense(const sattn_qkv_quant* qkv, int B, int H, int Lq, 
   const int qpw = attn_queries_per_wg();
   const int64_t ntile = ceil64(Lq) * 64 / qpw + (ceil64(Lq) * 64 % qpw != 0);
   const int64_t grid = 8 * (int64_t)((H + 7) / 8) * B * ntile;
-  if (grid > 0x7fffffff) return SATTN_EUNSUPPORTED;
+  if (grid > kMaxGroups256) return SATTN_EUNSUPPORTED;
   return launch_attention(p, grid, acc_out != nullptr, static_cast<hipStream_t>(stream)) == hipSuccess
              ? SATTN_OK
              : SATTN_EHIP;
@@ -222,7 +226,7 @@ sattn_status sattn_fwd_varlen(const sattn_qkv_quant* qkv, const int32_t* cu_seql
   p.max_kblocks = ceil64(k_clip);
   const int64_t tiles_bound = q_clip / attn_queries_per_wg() + nseg + 1;
   const int64_t grid = 8 * (int64_t)((H + 7) / 8) * tiles_bound;
-  if (grid > 0x7fffffff) return SATTN_EUNSUPPORTED;
+  if (grid > kMaxGroups256) return SATTN_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_plan(cu_seqlens_q, cu_seqlens_k, nseg, q_clip, k_clip, order, tpref, s) != hipSuccess) return SATTN_EHIP;
   return launch_attention(p, grid, false, s) == hipSuccess ? SATTN_OK : SATTN_EHIP;
@@ -262,7 +266,7 @@ sattn_status sattn_fwd_fused(const sattn_qkv_quant* kv, sattn_bf16_in q, const i
   const int qpw = attn_queries_per_wg();
   const int64_t grid = varlen ? 8 * (int64_t)((H + 7) / 8) * (Lq / qpw + nseg + 1)
                               : 8 * (int64_t)((H + 7) / 8) * nseg * ((ceil64(Lq) * 64 + qpw - 1) / qpw);
-  if (grid > 0x7fffffff) return SATTN_EUNSUPPORTED;
+  if (grid > kMaxGroups256) return SATTN_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (varlen) {
     p.order = static_cast<int32_t*>(workspace);

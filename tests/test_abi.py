@@ -119,6 +119,9 @@ def test_fwd_validation():
     assert f(ctypes.byref(_quant_struct(cap=0)), 2, 1, 64, 64, 128, 0.1, _out(), None) == B.SATTN_ENOSPACE
     assert f(None, 1, 1, 64, 64, 128, 0.1, _out(), None) == B.SATTN_EINVAL
     assert f(ctypes.byref(_quant_struct(rows=16)), 1, 1, 64, 64, 128, 0.1, _out(), None) == B.SATTN_EINVAL
+    # 2^31 - 1 queries of 8 heads: 1.3e8 workgroups, beyond one dispatch's 32-bit work-item count
+    assert f(ctypes.byref(_quant_struct(cap=1 << 40)), 1, 8, (1 << 31) - 1, 64, 128, 0.1, _out(), None) \
+        == B.SATTN_EUNSUPPORTED
     v = L.sattn_fwd_varlen
     assert v(ctypes.byref(q), FAKE, FAKE, 2, 100, 1, 128, 0.1, _out(), FAKE, 4, None) == B.SATTN_ENOSPACE
     assert v(ctypes.byref(q), None, FAKE, 2, 100, 1, 128, 0.1, _out(), FAKE, 1024, None) == B.SATTN_EINVAL
