@@ -342,6 +342,26 @@ def test_degenerate_values():
     assert np.all(got[0] == got[0, :1])
 
 
+@pytest.mark.parametrize("sm_scale", [1e-4, 1.0, 4.0])
+def test_extreme_softmax_scales(sm_scale):
+    """Nearly flat (sm_scale 1e-4: every P close to 1, O close to the mean of V) and sharply
+    peaked rows (1.0 and 4.0: score spans of tens to hundreds in base 2, so most P underflow
+    E4M3 and one or two keys carry each row), against the oracle."""
+    _need_gpu()
+    g = torch.Generator().manual_seed(13)
+    H, Lq, Lk = 2, 200, 333
+    q = torch.randn((1, Lq, H, 128), generator=g).to(torch.bfloat16)
+    k = torch.randn((1, Lk, H, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((1, Lk, H, 128), generator=g).to(torch.bfloat16)
+    quant = B.sattn_quantize_qkv(q.cuda(), k.cuda(), v.cuda())
+    out = B.sattn_fwd(quant, 1, H, Lq, Lk, sm_scale)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)[0]
+    oq = O.quantize(W.packed_float64(q), W.packed_float64(k), W.packed_float64(v), [0, Lq], [0, Lk])
+    ref = O.attention(oq, sm_scale)
+    _check_output(got, ref, f"sm_scale {sm_scale}")
+
+
 def test_thousand_launches_of_the_fixed_shape_agree():
     """The pages' fixed shape (B=1, H=1, 128 queries, 192 keys in three K64 epochs) run
     1,000 times back to back on one stream: every output identical to the first."""
