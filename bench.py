@@ -181,14 +181,18 @@ def cpu_oracle_full(w, inp):
         O.attention(O.quantize(q, k, v, inp["cu_q"], inp["cu_k"]), w.sm_scale)
         return time.perf_counter() - t0
 
-    run()  # warm-up (imports, first-touch)
-    t_all = min(run() for _ in range(3))
+    small = w.ops() <= 1e9
+    if small:
+        run()  # warm-up (imports, first-touch)
+    reps = 3 if small else 1
+    t_all = min(run() for _ in range(reps))
     with threadpool_limits(limits=1):
-        t_one = min(run() for _ in range(3))
+        t_one = min(run() for _ in range(reps))
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": t_all * 1e6, "unit": "us", "cores": threads, "kind": "oracle",
             "single_thread_us": t_one * 1e6,
-            "sample": "FP64 oracle, whole shape (quantize + attention), best of 3", "cpu": _cpu_model()}
+            "sample": f"FP64 oracle, whole shape (quantize + attention), {'best of 3' if small else 'one run'}",
+            "cpu": _cpu_model()}
 
 
 def latency(args, w, torch, B):
@@ -272,7 +276,7 @@ def latency(args, w, torch, B):
     if w.name == "fixed_q128_kv192":
         line["context"] = (f"pages, GB10: {PAGES_FIXED_SHAPE_US} us per launch p50 (same shape, 500 x 20 "
                            f"launches); vs_baseline = value / that")
-    if not args.no_cpu_baseline and w.ops() <= 1e9:  # larger shapes: the throughput mode's sampled baseline
+    if not args.no_cpu_baseline and w.ops() <= 1e11:  # larger shapes: the throughput mode's sampled baseline
         line["cpu_baseline"] = cpu_oracle_full(w, inp)
     print(json.dumps(line))
     if not replays_ok:
