@@ -15,7 +15,7 @@ from oracle.codecs import e4m3, fl32
 
 
 def _softmax_variant(d_no_alpha=False, alpha_inverted=False, old_max=False, ro_no_alpha=False, pad=False,
-                     epoch_override=None):
+                     epoch_override=None, scale_after_e4m3=False, d_from_p8=False):
     """The oracle's online recurrence with one deliberate error switched on."""
 
     def f(S, vvals, quantize_p=True, epoch=None, checkpoints=None):
@@ -35,8 +35,12 @@ def _softmax_variant(d_no_alpha=False, alpha_inverted=False, old_max=False, ro_n
             alpha = np.where(first, 0.0, np.exp2((m_new - m) if alpha_inverted else (m - m_new)))
             ref = np.where(first, m_new, m) if old_max else m_new
             Pe = np.exp2(Se - ref[:, None])
-            d = (d + np.sum(Pe, axis=1)) if d_no_alpha else (d * alpha + np.sum(Pe, axis=1))
-            Pq = e4m3(448.0 * Pe) if quantize_p else Pe
+            if scale_after_e4m3:  # quantized on [0, 1] (subnormals from 2^-6 down), then scaled
+                Pq = 448.0 * e4m3(Pe) if quantize_p else Pe
+            else:
+                Pq = e4m3(448.0 * Pe) if quantize_p else Pe
+            psum = np.sum(Pq, axis=1) / 448.0 if (d_from_p8 and quantize_p) else np.sum(Pe, axis=1)
+            d = (d + psum) if d_no_alpha else (d * alpha + psum)
             RO = (RO + Pq @ vvals[e0:e0 + epoch]) if ro_no_alpha else (RO * alpha[:, None] + Pq @ vvals[e0:e0 + epoch])
             m = m_new
             if checkpoints is not None:
@@ -44,6 +48,16 @@ def _softmax_variant(d_no_alpha=False, alpha_inverted=False, old_max=False, ro_n
         return RO, d
 
     return f
+
+
+def _quantize_v_per_head(v):
+    L, H, D = v.shape
+    amax = np.max(np.abs(v), axis=(0, 2))[:, None] * np.ones((1, D))  # one scale per head
+    safe = np.where(amax > 0, amax, 1.0)
+    inv = np.where(amax > 0, fl32(448.0 / safe), 0.0)
+    vals = e4m3(fl32(v * inv[None]))
+    from oracle.codecs import e4m3_encode
+    return e4m3_encode(vals), vals, np.where(amax > 0, fl32(safe / 448.0), 0.0)
 
 
 def _k_smooth_per_token(k):
@@ -171,6 +185,10 @@ MUTANTS = {
                             PINS_ATTN),
     "partial epoch padded with zero scores": (lambda mp: mp.setattr(O, "online_softmax_pv", _softmax_variant(pad=True)),
                                               PINS_ATTN),
+    "P quantized before the 448 scaling": (
+        lambda mp: mp.setattr(O, "online_softmax_pv", _softmax_variant(scale_after_e4m3=True)), PINS_ATTN),
+    "denominator summed from the quantized probabilities": (
+        lambda mp: mp.setattr(O, "online_softmax_pv", _softmax_variant(d_from_p8=True)), PINS_ATTN),
     "epoch of 32 keys": (lambda mp: (mp.setattr(O, "EPOCH", 32),
                                      mp.setattr(O, "online_softmax_pv", _softmax_variant(epoch_override=32))),
                          PINS_ATTN + [P.test_pages_shape_facts]),
@@ -178,6 +196,8 @@ MUTANTS = {
     "Q/K blocks of 32 tokens": (lambda mp: mp.setattr(O, "BLOCK", 32), PINS_QUANT),
     "INT8 ties away from zero": (lambda mp: mp.setattr(O, "rne", _rne_half_away), PINS_QUANT),
     "V scaled per token": (lambda mp: mp.setattr(O, "quantize_v", _quantize_v_per_token), PINS_QUANT),
+    "V scaled per head instead of per channel": (lambda mp: mp.setattr(O, "quantize_v", _quantize_v_per_head),
+                                                 PINS_QUANT),
     "Q and K exchanged in the scores": (lambda mp: mp.setattr(O, "scores", _scores_q_k_swapped), PINS_ATTN),
     "score scale without k_scale": (lambda mp: mp.setattr(O, "block_sigma", _block_sigma_without_k), PINS_ATTN),
     "softmax scale without log2 e": (lambda mp: mp.setattr(O, "sm_scale_log2", lambda s: float(fl32(np.float32(s)))),
