@@ -151,6 +151,35 @@ def test_output_within_tolerance(name):
     assert torch.isfinite(c["out"].float()).all()
 
 
+@pytest.mark.parametrize("name", NAMES)
+def test_quantization_error_against_exact_attention(name):
+    """A diagnostic of the method rather than of the kernel: the relative L2 distance of the
+    GPU output from textbook FP64 softmax attention on the same BF16 inputs (the pages'
+    own accuracy measure), printed beside the kernel's distance from the oracle, and held
+    to the oracle's own sanity bound of 5e-2.  The kernel's distance from the oracle must
+    be a small fraction of the method's distance from exact attention."""
+    c = case(name)
+    w, oq, inp = c["w"], c["oq"], c["inp"]
+    q64, k64, v64 = (W.packed_float64(inp[n]) for n in "qkv")
+    out = c["out"].float().cpu().numpy().astype(np.float64)
+    rows = {si: _sample_rows(seg["q8"].shape[0]) for si, seg in enumerate(oq)}
+    ref = O.attention(oq, w.sm_scale, rows=rows)
+    d_ex = d_or = n_ex = 0.0
+    for si, ((a, b), (ka, kb)) in enumerate(zip(O.segments(inp["cu_q"]), O.segments(inp["cu_k"]))):
+        if b == a or kb == ka:
+            continue
+        r = rows[si]
+        ex = O.softmax_attention_exact(q64[a:b][r], k64[ka:kb], v64[ka:kb], w.sm_scale)
+        got = (out[a:b] if w.varlen else out[si])[r]
+        d_ex += float(np.sum((got - ex) ** 2))
+        d_or += float(np.sum((got - ref[si]) ** 2))
+        n_ex += float(np.sum(ex ** 2))
+    rl2_exact, rl2_oracle = (d_ex / n_ex) ** 0.5, (d_or / n_ex) ** 0.5
+    _say(f"[diag] {name}: rel-L2 vs exact FP64 attention {rl2_exact:.4f}, vs the oracle {rl2_oracle:.2e}")
+    assert rl2_exact <= 5e-2
+    assert rl2_oracle <= 0.1 * rl2_exact
+
+
 # ---------------------------------------------------------------- per-warp (32-row) Q scales
 Q32_NAMES = ["fixed_q128_kv192", "ragged_b2_h16_l1000", "ragged_b2_h16_l2049", "varlen_h24_4seg"]
 
