@@ -304,6 +304,47 @@ def test_v_power_of_two_scaling_is_exact():
     assert torch.equal(out.float(), c["out"].float() * 8.0)
 
 
+def test_head_permutation_permutes_output():
+    """Heads are independent: permuting the heads of Q, K and V permutes the output heads
+    bit for bit (although other workgroups, on other XCDs, now compute each head)."""
+    _need_gpu()
+    g = torch.Generator().manual_seed(17)
+    H, L = 11, 333
+    q, k, v = (torch.randn((2, L, H, 128), generator=g).to(torch.bfloat16).cuda() for _ in range(3))
+    perm = torch.randperm(H, generator=g).cuda()
+    out = B.sattn_fwd(B.sattn_quantize_qkv(q, k, v), 2, H, L, L, 0.09)
+    qp, kp, vp = (t[:, :, perm] for t in (q, k, v))  # strided views: the head stride is not H*D
+    outp = B.sattn_fwd(B.sattn_quantize_qkv(*(t.contiguous() for t in (qp, kp, vp))), 2, H, L, L, 0.09)
+    torch.cuda.synchronize()
+    assert torch.equal(outp, out[:, :, perm])
+
+
+def test_k_mean_shift_changes_nothing_on_the_gpu():
+    """K -> K + b with a dyadic per-(head, channel) b, K on a 1/16 grid and L a power of two,
+    so every mean and every K - mean is exact: the INT8 K codes and scales, the INT32
+    scores and the output are bit-identical (the K-smoothing invariance, on the GPU)."""
+    _need_gpu()
+    g = torch.Generator().manual_seed(19)
+    H, L = 3, 256
+    q = torch.randn((1, L, H, 128), generator=g).to(torch.bfloat16)
+    k = (torch.randint(-128, 128, (1, L, H, 128), generator=g) / 16.0).to(torch.bfloat16)
+    v = torch.randn((1, L, H, 128), generator=g).to(torch.bfloat16)
+    b = (torch.randint(-64, 65, (H, 128), generator=g) / 16.0)
+    k2 = (k.float() + b).to(torch.bfloat16)
+    assert torch.equal(k2.float(), k.float() + b)  # still exact in BF16
+    qa, qb = (B.sattn_quantize_qkv(q.cuda(), kk.cuda(), v.cuda()) for kk in (k, k2))
+    torch.cuda.synchronize()
+    assert torch.equal(qb.k_mean.cpu(), qa.k_mean.cpu() + b[None])
+    nb = L // 64  # the blocks written (the buffers hold one more of capacity, never written)
+    assert torch.equal(qb.k[:, :nb], qa.k[:, :nb]) and torch.equal(qb.k_scale[:, :nb], qa.k_scale[:, :nb])
+    for h in range(H):
+        acc_a, s_a, out_a = B.sattn_debug_scores(qa, 1, H, L, L, 0.0884, 0, h)
+        acc_b, s_b, out_b = B.sattn_debug_scores(qb, 1, H, L, L, 0.0884, 0, h)
+        torch.cuda.synchronize()
+        assert torch.equal(acc_a, acc_b) and torch.equal(s_a, s_b)
+        assert torch.equal(out_a[:, :, h], out_b[:, :, h])
+
+
 def test_repeated_launches_are_bitwise_identical():
     c = case("dense_h8_l4096")
     w = c["w"]
