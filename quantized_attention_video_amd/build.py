@@ -39,5 +39,26 @@ def build(verbose=False):
     return LIB
 
 
+C_DRIVER_SRC = os.path.join(ROOT, "tests", "c_abi_driver.cpp")
+C_DRIVER = os.path.join(ROOT, "tests", "c_abi_driver")
+
+
+def build_c_driver(verbose=False):
+    """Compile the test program that calls the library through include/sattn.h alone (host
+    code, linked against LIB with a path relative to itself)."""
+    tmp = C_DRIVER + ".tmp"
+    cmd = ["hipcc", "-O2", "-std=c++17", "-Wall", "-I", os.path.join(ROOT, "include"), C_DRIVER_SRC, "-L", HERE,
+           "-lsattn", "-Wl,-rpath,$ORIGIN/../quantized_attention_video_amd", "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if "--hip-link" not in ln and ln.strip()]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc (C ABI test driver) failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs), file=sys.stderr)
+    os.replace(tmp, C_DRIVER)
+    return C_DRIVER
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_driver(verbose=True))
