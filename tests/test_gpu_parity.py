@@ -345,6 +345,66 @@ def test_k_mean_shift_changes_nothing_on_the_gpu():
         assert torch.equal(out_a[:, :, h], out_b[:, :, h])
 
 
+def test_two_streams_at_once_match_one_after_the_other():
+    """The library keeps no state between calls: two problems quantized and attended on two
+    streams at the same time give the same bits as the same calls made one after another."""
+    _need_gpu()
+    g = torch.Generator().manual_seed(31)
+    probs = []
+    for H, L in ((4, 700), (3, 1100)):
+        probs.append(tuple(torch.randn((1, L, H, 128), generator=g).to(torch.bfloat16).cuda() for _ in range(3)))
+
+    def run(p):
+        q, k, v = p
+        H, L = q.shape[2], q.shape[1]
+        return B.sattn_fwd(B.sattn_quantize_qkv(q, k, v), 1, H, L, L, 0.09)
+
+    seq = [run(p) for p in probs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    outs = [None, None]
+    for _ in range(3):
+        for i, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                outs[i] = run(probs[i])
+        torch.cuda.synchronize()
+        assert all(torch.equal(o, r) for o, r in zip(outs, seq))
+
+
+def test_quantize_and_forward_replay_from_a_captured_graph():
+    """The whole step captured in one HIP graph (no memset nodes: the library issues none)
+    and replayed with new inputs copied into the captured buffers: every replay equals the
+    eager result for those inputs, with eager work and synchronisations in between."""
+    _need_gpu()
+    g = torch.Generator().manual_seed(37)
+    H, L = 3, 600
+    q, k, v = (torch.randn((1, L, H, 128), generator=g).to(torch.bfloat16).cuda() for _ in range(3))
+    quant = B.sattn_quantize_qkv(q, k, v)  # buffers reused by the captured calls
+    out = torch.empty((1, L, H, 128), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture stream's side, as torch recommends
+        B.sattn_quantize_qkv(q, k, v, out=quant)
+        B.sattn_fwd(quant, 1, H, L, L, 0.09, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.sattn_quantize_qkv(q, k, v, out=quant)
+        B.sattn_fwd(quant, 1, H, L, L, 0.09, out=out)
+    for _ in range(3):
+        new = [torch.randn((1, L, H, 128), generator=g).to(torch.bfloat16).cuda() for _ in range(3)]
+        ref = B.sattn_fwd(B.sattn_quantize_qkv(*new), 1, H, L, L, 0.09)  # eager, fresh buffers
+        torch.cuda.synchronize()
+        for dst, src in zip((q, k, v), new):
+            dst.copy_(src)
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+
+
 def test_repeated_launches_are_bitwise_identical():
     c = case("dense_h8_l4096")
     w = c["w"]
