@@ -17,6 +17,8 @@ Where the pages leave a step open, the plainest reading is taken:
     rows (the rows one of four QK warps owns in a 128-query tile), K staying per 64;
   * V is quantized per (sequence, head, channel): scale fl32(amax/448), multiply by
     fl32(448/amax), E4M3 RNE;
+  * a Q/K block or V channel whose amax is 0, or so small that its binary32 reciprocal
+    overflows (fl32(127/amax) or fl32(448/amax) = inf), gets scale 0 and zero codes;
   * sm_scale and log2(e) are folded into the per-block score scale
     sigma = fl32(fl32(q_scale * c) * k_scale) with c = fl32(sm_scale * log2 e);
   * the score is fl32(acc * sigma), acc the exact integer dot product;
@@ -61,7 +63,9 @@ def quantize_int8_blocks(x, block=None):
     binary32 operation: the float64 quotient of two binary32 operands rounded again to
     binary32 equals the correctly rounded binary32 quotient, because 53 >= 2*24 + 2.
     x*inv is exact in float64 (24 + 24 bits), so fl32 applies the single rounding.
-    An all-zero block gets scale 0 and codes 0.
+    An all-zero block gets scale 0 and codes 0, and so does a block whose amax is too
+    small for a finite binary32 reciprocal (fl32(127/amax) = inf, amax < 127/FLT_MAX,
+    about 3.7e-37): the pages leave it open, and x*inf would make NaN codes.
     """
     block = BLOCK if block is None else block
     L, H, D = x.shape
@@ -71,10 +75,12 @@ def quantize_int8_blocks(x, block=None):
     for b in range(nblk):
         blk = x[b * block:(b + 1) * block]  # [n, H, D]; the last block may be partial
         amax = np.max(np.abs(blk), axis=(0, 2))  # [H]
-        nz = amax > 0
-        safe = np.where(nz, amax, 1.0)
+        safe = np.where(amax > 0, amax, 1.0)
+        with np.errstate(over="ignore"):
+            inv_all = fl32(127.0 / safe)
+        nz = (amax > 0) & np.isfinite(inv_all)
         scale = np.where(nz, fl32(safe / 127.0), 0.0)
-        inv = np.where(nz, fl32(127.0 / safe), 0.0)
+        inv = np.where(nz, inv_all, 0.0)
         q = np.clip(rne(fl32(blk * inv[None, :, None])), -127.0, 127.0)
         codes[b * block:(b + 1) * block] = q
         scales[:, b] = scale
@@ -104,10 +110,12 @@ def quantize_v(v):
     """
     L, H, D = v.shape
     amax = np.max(np.abs(v), axis=0) if L else np.zeros((H, D))
-    nz = amax > 0
-    safe = np.where(nz, amax, 1.0)
+    safe = np.where(amax > 0, amax, 1.0)
+    with np.errstate(over="ignore"):
+        inv_all = fl32(448.0 / safe)
+    nz = (amax > 0) & np.isfinite(inv_all)  # as for INT8: no finite reciprocal, a zero channel
     scale = np.where(nz, fl32(safe / 448.0), 0.0)
-    inv = np.where(nz, fl32(448.0 / safe), 0.0)
+    inv = np.where(nz, inv_all, 0.0)
     vals = e4m3(fl32(v * inv[None]))
     return e4m3_encode(vals), vals, scale
 

@@ -510,8 +510,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   if constexpr (KSL) c.ks_next = nkb > 0 ? g_ks[0] : 0.f;
   if (fused_q && c.active) {  // the quantizer's arithmetic: fl32 scale, RNE codes in [-127, 127]
     const float amax = p.q_scale_shift ? qamax : fmaxf(qamax, g_qamax[wave ^ 1]);
-    const float scale = amax > 0.f ? amax / 127.0f : 0.f;
-    const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+    const float rcp = 127.0f / amax;
+    const bool zero = !(amax > 0.f) || isinf(rcp);  // the quantizer's zero-block rule
+    const float scale = zero ? 0.f : amax / 127.0f;
+    const float inv = zero ? 0.f : rcp;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll

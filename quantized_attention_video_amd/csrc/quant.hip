@@ -77,8 +77,11 @@ __device__ __forceinline__ void emit_qk(const BlockRows& b, const float* mu, int
   float scale[2], inv[2];
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
-    scale[f] = am[f] > 0.f ? am[f] / 127.0f : 0.f;
-    inv[f] = am[f] > 0.f ? 127.0f / am[f] : 0.f;
+    inv[f] = 127.0f / am[f];
+    // amax 0, or so small that the reciprocal overflows: a zero block (scale 0, codes 0)
+    const bool zero = !(am[f] > 0.f) || isinf(inv[f]);
+    scale[f] = zero ? 0.f : am[f] / 127.0f;
+    inv[f] = zero ? 0.f : inv[f];
   }
   const int cbase = 8 * c8, g2 = cbase >> 6, u = (cbase & 63) >> 4, s0 = cbase & 15;
 #pragma unroll
@@ -272,8 +275,10 @@ __global__ __launch_bounds__(kD * kFinParts) void finalize_kernel(SegGeom gk, in
   const SegInfo ki = seg_info(gk, s, 0);
   const int64_t o = ((int64_t)s * H + h) * kD + c;
   k_mean[o] = ki.len > 0 ? (float)(sum / (double)ki.len) : 0.f;
-  v_scale[o] = amax > 0.f ? amax / 448.0f : 0.f;
-  v_inv[o] = amax > 0.f ? 448.0f / amax : 0.f;
+  const float inv = 448.0f / amax;
+  const bool zero = !(amax > 0.f) || isinf(inv);  // as for INT8 blocks: a zero channel
+  v_scale[o] = zero ? 0.f : amax / 448.0f;
+  v_inv[o] = zero ? 0.f : inv;
 }
 
 // ---------------------------------------------------------------------------- K and V

@@ -492,6 +492,38 @@ def test_extreme_softmax_scales(sm_scale):
     _check_output(got, ref, f"sm_scale {sm_scale}")
 
 
+def test_blocks_too_small_for_a_finite_reciprocal():
+    """Values at the bottom of the binary32 range (a Q block, all of one segment's K, a V
+    channel below ~1e-36, where 127/amax or 448/amax overflows): zero blocks and channels,
+    byte for byte as the oracle; the fused-Q forward agrees; the output stays finite."""
+    _need_gpu()
+    g = torch.Generator().manual_seed(41)
+    H, L = 2, 200
+    q = torch.randn((2, L, H, 128), generator=g)
+    k = torch.randn((2, L, H, 128), generator=g)
+    v = torch.randn((2, L, H, 128), generator=g)
+    q[0, 64:128] *= 1e-38  # one Q block
+    k[1] *= 1e-38          # all of segment 1's K: mean and smoothed K that small too
+    v[0, :, :, 9] *= 1e-37  # one V channel
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    quant = B.sattn_quantize_qkv(qd, kd, vd)
+    out = B.sattn_fwd(quant, 2, H, L, L, 0.0884)
+    kv = B.sattn_quantize_kv(qd, kd, vd)
+    fused = B.sattn_fwd_fused(kv, qd, 0.0884, Lk=L)
+    torch.cuda.synchronize()
+    cu = [0, L, 2 * L]
+    oq = O.quantize(W.packed_float64(q), W.packed_float64(k), W.packed_float64(v), cu, cu)
+    assert oq[0]["q_scale"][0, 1] == 0 and not oq[1]["k_scale"].any() and oq[0]["v_scale"][0, 9] == 0
+    _assert_quantized_equal(quant, oq, B.segment_blocks(cu, L), B.segment_blocks(cu, L), H)
+    assert torch.equal(fused, out)
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    ref = O.attention(oq, 0.0884)
+    for si in range(2):
+        _check_output(got[si], ref[si * L:(si + 1) * L], f"tiny values seg {si}")
+
+
 def test_thousand_launches_of_the_fixed_shape_agree():
     """The pages' fixed shape (B=1, H=1, 128 queries, 192 keys in three K64 epochs) run
     1,000 times back to back on one stream: every output identical to the first."""

@@ -157,6 +157,28 @@ def test_zero_blocks_and_channels():
     assert np.all(v8 == 0) and np.all(vs == 0)
 
 
+def test_blocks_too_small_for_a_finite_reciprocal_are_zero():
+    """The edge of the binary32 range, where 127/amax (448/amax for V) overflows: such a
+    block or channel is a zero one (scale 0, codes 0), while one just above the edge is
+    quantized as usual (its largest value at code 127, or at E4M3 448)."""
+    flt_max = float(np.finfo(np.float32).max)
+    edge_q, edge_v = 127.0 / flt_max, 448.0 / flt_max  # about 3.7e-37 and 1.3e-36
+    x = np.zeros((128, 1, 128))
+    x[0, 0, 0], x[1, 0, 5] = bf16(0.5 * edge_q), -bf16(0.25 * edge_q)  # block 0: below the edge
+    x[64, 0, 3] = bf16(4.0 * edge_q)  # block 1: above it
+    x[65, 0, 7] = -bf16(2.0 * edge_q)
+    codes, scales = O.quantize_int8_blocks(x)
+    assert scales[0, 0] == 0 and not codes[:64].any()
+    assert scales[0, 1] == fl32(bf16(4.0 * edge_q) / 127.0) > 0
+    assert codes[64, 0, 3] == 127 and codes[65, 0, 7] == -64
+    v = np.zeros((10, 1, 128))
+    v[:, 0, 0] = bf16(0.5 * edge_v) * np.linspace(-1, 1, 10)  # channel 0: below the edge
+    v[:, 0, 1] = bf16(4.0 * edge_v) * np.linspace(-1, 1, 10)  # channel 1: above it
+    v8, vals, vs = O.quantize_v(v)
+    assert vs[0, 0] == 0 and not np.any(vals[:, 0, 0])
+    assert vs[0, 1] > 0 and np.max(np.abs(vals[:, 0, 1])) == 448.0
+
+
 def test_v_channel_scale_exact_case():
     v = np.zeros((10, 1, 128))
     v[:, 0, 5] = np.arange(10) * 0.25  # amax 2.25 -> scale fl32(2.25/448), inv fl32(448/2.25)
