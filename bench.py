@@ -23,6 +23,11 @@ launches are replayed from a captured HIP graph so that host enqueue time (Pytho
 ctypes) does not stretch the interval, with the eager figure beside it.  Its CPU baseline
 is the whole oracle on the whole shape, on one host thread and on all of them.
 
+--summarize-trace CSV (with the --steps/--warmup of the profiled run) reads a rocprofv3
+kernel-trace CSV of a bench.py run and prints per-kernel launch statistics with the warm-up
+launches and the timed ones apart; --summarize-counters CSV [CSV ...] prints the mean of
+every counter of rocprofv3 --pmc runs per kernel over the timed launches.
+
 --fused-q times the other form of the same path: sattn_quantize_qkv for K and V only, then
 sattn_fwd_fused, which quantizes Q inside the attention launch from the BF16 view (the
 outputs are bit-identical).  Its roofline entry carries no traffic figure: the committed
@@ -283,6 +288,48 @@ def latency(args, w, torch, B):
         raise SystemExit("graph replays differ from the eager output")
 
 
+def _short(name):
+    """A kernel's name without namespace and argument list (templates kept)."""
+    n = name.split("(")[0]
+    return n.replace("sattn::", "")
+
+
+def summarize_trace(path, steps, warmup):
+    """Per-kernel launch times of a rocprofv3 kernel trace of bench.py: the first `warmup`
+    launches of each step kernel are the warm-up, the next `steps` the timed ones."""
+    import csv
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    by = {}
+    for r in rows:
+        by.setdefault(_short(r["Kernel_Name"]), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print(f"{'kernel':44s} {'phase':7s} {'calls':>5s} {'avg_us':>10s} {'p50_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+    for k, us in by.items():
+        parts = [("all", us)]
+        if len(us) == steps + warmup:
+            parts = [("warm-up", us[:warmup]), ("timed", us[warmup:])]
+        for label, xs in parts:
+            if xs:
+                print(f"{k[:44]:44s} {label:7s} {len(xs):5d} {sum(xs) / len(xs):10.1f} {_pct(xs, 50):10.1f} "
+                      f"{min(xs):10.1f} {max(xs):10.1f}")
+
+
+def summarize_counters(paths, steps, warmup):
+    """Mean of every rocprofv3 --pmc counter per kernel (summed over the dimensions a counter
+    reports per dispatch), over the timed launches of the step kernels (the last `steps`)."""
+    import csv
+    per = {}  # (kernel, counter) -> {dispatch: value}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            key = (_short(r["Kernel_Name"]), r["Counter_Name"])
+            d = per.setdefault(key, {})
+            d[int(r["Dispatch_Id"])] = d.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
+    for (k, cn), d in sorted(per.items()):
+        vals = [d[i] for i in sorted(d)]
+        if len(vals) == steps + warmup:
+            vals = vals[warmup:]
+        print(f"{k[:44]:44s} {cn:28s} n={len(vals):3d} mean={sum(vals) / len(vals):.6g}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -297,7 +344,15 @@ def main():
     ap.add_argument("--samples", type=int, default=500, help="--latency: samples of 20 launches")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run N plain 1 GiB device copies (counter calibration) and exit")
+    ap.add_argument("--summarize-trace", metavar="CSV", help="print launch statistics of a rocprofv3 kernel trace")
+    ap.add_argument("--summarize-counters", metavar="CSV", nargs="+", help="print per-kernel counter means")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.steps, args.warmup)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.steps, args.warmup)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -412,6 +467,7 @@ def main():
             "traffic": traffic,
             "ops_per_launch": ops,
             "avg_launch_ms": fwd_avg,
+            "attn_hip_sha256_16": kernel_source_hash(),
         },
         "breakdown": {
             "fwd_ms_avg": fwd_avg,

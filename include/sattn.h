@@ -181,27 +181,58 @@ SATTN_API sattn_status sattn_fwd(const sattn_qkv_quant* qkv, int B, int H, int L
 /*
  * sattn_fwd_varlen — block-diagonal (per-segment) version of sattn_fwd for packed
  * sequences; cu_seqlens_q/k are the same device arrays given to sattn_quantize_qkv.
- * total_q is the number of packed query tokens the output view holds (rows past it are
- * never written).  `workspace` (fwd_workspace_bytes, 16-byte aligned) receives the
+ * total_q and total_k are the packed query and key tokens the views held: rows past
+ * total_q are never written, and a segment reaching past total_k keys is clipped there,
+ * exactly as sattn_quantize_qkv clipped it (its keys past the K/V views were never
+ * quantized).  `workspace` (fwd_workspace_bytes, 16-byte aligned) receives the
  * longest-first schedule of the segments and is scratch for the caller.
  */
 SATTN_API sattn_status sattn_fwd_varlen(const sattn_qkv_quant* qkv, const int32_t* cu_seqlens_q,
-                              const int32_t* cu_seqlens_k, int nseg, int64_t total_q, int H, int D,
-                              float sm_scale, sattn_bf16_out o, void* workspace, size_t workspace_bytes,
-                              void* stream);
+                              const int32_t* cu_seqlens_k, int nseg, int64_t total_q, int64_t total_k, int H,
+                              int D, float sm_scale, sattn_bf16_out o, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Checkpoint buffers of sattn_debug_scores: caller-owned device memory; any pointer may be
+ * NULL to skip that checkpoint.  Row r of each buffer belongs to the r-th sampled query row
+ * (see sattn_debug_scores).  Keys and epochs are numbered within the segment. */
+typedef struct {
+  int32_t* acc;   /* [rows][ld]: the exact INT32 accumulator sum_c q8[i,c] k8[j,c] of key j   */
+  float* s;       /* [rows][ld]: the FP32 score fl32(acc * sigma) of key j (base-2 units)    */
+  int64_t ld;     /* row stride of acc and s in elements; keys j >= ld are not written        */
+  float* m;       /* [rows][nep]: running max m after epoch e                                 */
+  float* d;       /* [rows][nep]: running denominator after epoch e, in units of 448 P (the
+                     sum of the unquantized 448 * 2^(S - m) values, FP32)                      */
+  float* alpha;   /* [rows][nep]: epoch e's rescale factor 2^(m_{e-1} - m_e) (0 for e = 0)     */
+  uint8_t* p8;    /* [rows][nep][64]: epoch e's E4M3 probability bytes e4m3(448 P), key
+                     64e + k at index k (keys past the segment's end hold 0)                  */
+  float* ro;      /* [rows][nep][128]: the running output RO = sum_j e4m3(448 P_j) * v8_j
+                     (v8_j the E4M3 code values; the FP32 accumulators) after epoch e          */
+  int64_t nep;    /* epochs recorded: e < nep (later epochs are not written)                  */
+} sattn_checkpoints;
 
 /*
- * sattn_debug_scores — checkpoint dump for one (segment, head) of a dense problem
- * (the Phase 2B report's "INT32-to-FP32 QK scores" checkpoint).  Runs the same
- * forward kernel as sattn_fwd with a dump enabled and writes, for every query row
- * i < Lq and key j < Lk of segment `seg`, head `head`:
- *   acc_out[i*Lk + j] = the exact INT32 accumulator, s_out[i*Lk + j] = fl32(acc*sigma).
- * Both buffers are device memory of Lq*Lk elements.  The forward output is written to
- * `o` exactly as sattn_fwd would for that (segment, head).
+ * sattn_debug_scores — the checkpoints of the Phase 2B report's "Exactness" section
+ * (INT32-to-FP32 QK scores, per-epoch m and d, E4M3 probability words, FP32 rescale
+ * values, the running output) for sampled query rows of one (segment, head).  It runs the
+ * forward kernel's own instantiation (the same tiles, pipeline and K-scale path as
+ * sattn_fwd / sattn_fwd_varlen for this problem) with stores of the checkpoint
+ * quantities added, for the query tiles that hold sampled rows only.
+ *
+ *   dense  (cu_seqlens_q == cu_seqlens_k == NULL): nseg segments of Lq queries and Lk keys.
+ *   varlen (both non-NULL): the device arrays given to sattn_quantize_qkv; Lq and Lk are
+ *          the packed query and key tokens the views held.
+ *
+ * Sampled rows: segment-relative query rows q_begin + i*q_step (i = 0, 1, ...) below both
+ * q_end and the segment's length; buffer row i belongs to the i-th of them, so every
+ * buffer needs ceil((q_end - q_begin) / q_step) rows.  `o` receives the forward output of
+ * the sampled rows of head `head` (bit-identical to sattn_fwd's), and no other element.
+ * Returns SATTN_EINVAL for seg/head out of range, q_begin < 0, q_end <= q_begin,
+ * q_step < 1, a NULL `ck`, ld < 1 with acc or s given, or nep < 1 with a per-epoch buffer.
  */
-SATTN_API sattn_status sattn_debug_scores(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D,
-                                float sm_scale, int seg, int head, int32_t* acc_out, float* s_out,
-                                sattn_bf16_out o, void* stream);
+SATTN_API sattn_status sattn_debug_scores(const sattn_qkv_quant* qkv, const int32_t* cu_seqlens_q,
+                                const int32_t* cu_seqlens_k, int nseg, int64_t Lq, int64_t Lk, int H, int D,
+                                float sm_scale, int seg, int head, int64_t q_begin, int64_t q_end,
+                                int64_t q_step, const sattn_checkpoints* ck, sattn_bf16_out o, void* stream);
 
 /*
  * sattn_fwd_fused — the forward with the Q preparation fused into the attention launch

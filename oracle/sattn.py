@@ -238,16 +238,6 @@ def softmax_attention_exact(q, k, v, sm_scale):
     return o
 
 
-def dequantized_inputs(seg):
-    """The values the quantized program multiplies, per segment: Q8*sq, K8*sk, V8*sv."""
-    L, H, D = seg["q8"].shape
-    qrep = np.repeat(seg["q_scale"], seg.get("q_rows", BLOCK), axis=1)[:, :L].T  # [L, H]
-    Lk = seg["k8"].shape[0]
-    krep = np.repeat(seg["k_scale"], BLOCK, axis=1)[:, :Lk].T
-    return (seg["q8"] * qrep[:, :, None], seg["k8"] * krep[:, :, None],
-            seg["v8val"] * seg["v_scale"][None])
-
-
 def rel_l2(a, b):
     """||a - b|| / ||b|| over all elements."""
     return float(np.linalg.norm((a - b).ravel()) / max(np.linalg.norm(b.ravel()), 1e-300))

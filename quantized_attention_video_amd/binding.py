@@ -42,6 +42,12 @@ class QKVQuant(ctypes.Structure):
                 ("q_scale_rows", ctypes.c_int32)]
 
 
+class Checkpoints(ctypes.Structure):
+    _fields_ = [("acc", ctypes.c_void_p), ("s", ctypes.c_void_p), ("ld", ctypes.c_int64), ("m", ctypes.c_void_p),
+                ("d", ctypes.c_void_p), ("alpha", ctypes.c_void_p), ("p8", ctypes.c_void_p), ("ro", ctypes.c_void_p),
+                ("nep", ctypes.c_int64)]
+
+
 class Sizes(ctypes.Structure):
     _fields_ = [("qblk_cap", ctypes.c_int64), ("kblk_cap", ctypes.c_int64), ("q_bytes", ctypes.c_size_t),
                 ("q_scale_bytes", ctypes.c_size_t), ("k_bytes", ctypes.c_size_t),
@@ -65,16 +71,17 @@ def lib():
         L.sattn_quantize_qkv.argtypes = [BF16In, BF16In, BF16In, i32, i32, i32, i64, i64, vp, vp,
                                          ctypes.POINTER(QKVQuant), vp, ctypes.c_size_t, vp]
         L.sattn_fwd.argtypes = [ctypes.POINTER(QKVQuant), i32, i32, i32, i32, i32, f32, BF16Out, vp]
-        L.sattn_fwd_varlen.argtypes = [ctypes.POINTER(QKVQuant), vp, vp, i32, i64, i32, i32, f32, BF16Out, vp,
+        L.sattn_fwd_varlen.argtypes = [ctypes.POINTER(QKVQuant), vp, vp, i32, i64, i64, i32, i32, f32, BF16Out, vp,
                                        ctypes.c_size_t, vp]
-        L.sattn_debug_scores.argtypes = [ctypes.POINTER(QKVQuant), i32, i32, i32, i32, i32, f32, i32, i32, vp, vp,
-                                         BF16Out, vp]
+        L.sattn_debug_scores.argtypes = [ctypes.POINTER(QKVQuant), vp, vp, i32, i64, i64, i32, i32, f32, i32, i32, i64,
+                                         i64, i64, ctypes.POINTER(Checkpoints), BF16Out, vp]
         L.sattn_fwd_fused.argtypes = [ctypes.POINTER(QKVQuant), BF16In, vp, vp, i32, i32, i64, i64, i32, f32,
                                       BF16Out, vp, ctypes.c_size_t, vp]
         L.sattn_status_string.argtypes = [i32]
         L.sattn_status_string.restype = ctypes.c_char_p
-        for name in EXPORTED[:-1]:
-            getattr(L, name).restype = ctypes.c_int32
+        for name in EXPORTED:
+            if name != "sattn_status_string":
+                getattr(L, name).restype = ctypes.c_int32
         _lib = L
     return _lib
 
@@ -132,6 +139,8 @@ class Quantized:
     H: int
     sizes: Sizes
     q_scale_rows: int = 64  # query rows per Q scale: 64 or 32 (q_scale is [H, qblk_cap * 64 / rows])
+    total_q: int = 0  # query and key tokens the buffers were sized for (packed: the views' lengths)
+    total_k: int = 0
 
     def struct(self):
         return QKVQuant(_ptr(self.q), _ptr(self.q_scale), self.k.data_ptr(), self.k_scale.data_ptr(),
@@ -155,7 +164,8 @@ def alloc_quantized(nseg, total_q, total_k, H, device="cuda", q_scale_rows=64, w
         v=torch.empty((H, s.kblk_cap, 8192), dtype=torch.uint8, **e),
         v_scale=torch.empty((nseg, H, D), dtype=torch.float32, **e),
         workspace=torch.empty(max(s.quant_workspace_bytes, 16), dtype=torch.uint8, **e),
-        qblk_cap=s.qblk_cap, kblk_cap=s.kblk_cap, nseg=nseg, H=H, sizes=s, q_scale_rows=q_scale_rows)
+        qblk_cap=s.qblk_cap, kblk_cap=s.kblk_cap, nseg=nseg, H=H, sizes=s, q_scale_rows=q_scale_rows,
+        total_q=total_q, total_k=total_k)
 
 
 def sattn_quantize_qkv(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, out=None, stream=None, q_scale_rows=64):
@@ -174,7 +184,8 @@ def sattn_quantize_qkv(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, out=None, 
         Lk = k.shape[1]
         total_q, total_k = nseg * Lq, nseg * Lk
     if out is None:
-        out = alloc_quantized(nseg, total_q, total_k, H, device=q.device, q_scale_rows=q_scale_rows)
+        with torch.cuda.stream(stream or torch.cuda.current_stream()):  # allocated on the stream that uses it
+            out = alloc_quantized(nseg, total_q, total_k, H, device=q.device, q_scale_rows=q_scale_rows)
     st = out.struct()
     qv = _view(q, BF16In) if out.q is not None else BF16In(0, 0, 0, 0)
     _check(lib().sattn_quantize_qkv(qv, _view(k, BF16In), _view(v, BF16In), nseg, H, D, Lq, Lk,
@@ -184,10 +195,17 @@ def sattn_quantize_qkv(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, out=None, 
     return out
 
 
+def _on(stream):
+    """Allocate temporaries on the stream the library call runs on (the caching allocator
+    then never hands their memory to other work while that stream still uses it)."""
+    return torch.cuda.stream(stream or torch.cuda.current_stream())
+
+
 def sattn_fwd(quant, B, H, Lq, Lk, sm_scale, out=None, stream=None):
     """Dense forward; returns (or fills) a BF16 [B, Lq, H, D] tensor (any strided view works)."""
     if out is None:
-        out = torch.empty((B, Lq, H, D), dtype=torch.bfloat16, device=quant.q.device)
+        with _on(stream):
+            out = torch.empty((B, Lq, H, D), dtype=torch.bfloat16, device=quant.q.device)
     st = quant.struct()
     _check(lib().sattn_fwd(ctypes.byref(st), B, H, Lq, Lk, D, float(sm_scale), _view(out, BF16Out),
                            _stream(stream)), "sattn_fwd")
@@ -204,7 +222,8 @@ def sattn_quantize_kv(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, stream=None
     else:
         nseg, H = q.shape[0], q.shape[2]
         total_q, total_k = nseg * q.shape[1], nseg * k.shape[1]
-    out = alloc_quantized(nseg, total_q, total_k, H, device=k.device, q_scale_rows=q_scale_rows, with_q=False)
+    with _on(stream):
+        out = alloc_quantized(nseg, total_q, total_k, H, device=k.device, q_scale_rows=q_scale_rows, with_q=False)
     return sattn_quantize_qkv(q, k, v, cu_seqlens_q, cu_seqlens_k, out=out, stream=stream)
 
 
@@ -219,13 +238,15 @@ def sattn_fwd_fused(kv, q, sm_scale, cu_seqlens_q=None, cu_seqlens_k=None, Lk=No
     if varlen:
         nseg, Lq, H = cu_seqlens_q.numel() - 1, q.shape[0], q.shape[1]
         if workspace is None:
-            workspace = fwd_workspace(nseg, device=q.device)
+            with _on(stream):
+                workspace = fwd_workspace(nseg, device=q.device)
         ws, wsb = workspace.data_ptr(), workspace.numel()
     else:
         nseg, Lq, H = q.shape[0], q.shape[1], q.shape[2]
         ws, wsb = None, 0
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        with _on(stream):
+            out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     st = kv.struct()
     _check(lib().sattn_fwd_fused(ctypes.byref(st), _view(q, BF16In), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), nseg, H,
                                  Lq, Lk, D, float(sm_scale), _view(out, BF16Out), ws, wsb, _stream(stream)),
@@ -238,32 +259,63 @@ def fwd_workspace(nseg, device="cuda"):
     return torch.empty(s.fwd_workspace_bytes, dtype=torch.uint8, device=device)
 
 
-def sattn_fwd_varlen(quant, cu_seqlens_q, cu_seqlens_k, total_q, sm_scale, out=None, workspace=None, stream=None):
-    """Packed forward; returns (or fills) a BF16 [total_q, H, D] tensor."""
+def sattn_fwd_varlen(quant, cu_seqlens_q, cu_seqlens_k, total_q, sm_scale, out=None, workspace=None, stream=None,
+                     total_k=None):
+    """Packed forward; returns (or fills) a BF16 [total_q, H, D] tensor.  total_k (the packed
+    key tokens the K/V views held) defaults to what `quant` was sized for."""
     nseg = cu_seqlens_q.numel() - 1
     H = quant.H
-    if out is None:
-        out = torch.empty((total_q, H, D), dtype=torch.bfloat16, device=quant.q.device)
-    if workspace is None:
-        workspace = fwd_workspace(nseg, device=quant.q.device)
+    total_k = quant.total_k if total_k is None else total_k
+    with _on(stream):
+        if out is None:
+            out = torch.empty((total_q, H, D), dtype=torch.bfloat16, device=quant.k.device)
+        if workspace is None:
+            workspace = fwd_workspace(nseg, device=quant.k.device)
     st = quant.struct()
-    _check(lib().sattn_fwd_varlen(ctypes.byref(st), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), nseg, total_q, H, D,
-                                  float(sm_scale), _view(out, BF16Out), workspace.data_ptr(), workspace.numel(),
+    _check(lib().sattn_fwd_varlen(ctypes.byref(st), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), nseg, total_q, total_k, H,
+                                  D, float(sm_scale), _view(out, BF16Out), workspace.data_ptr(), workspace.numel(),
                                   _stream(stream)), "sattn_fwd_varlen")
     return out
 
 
-def sattn_debug_scores(quant, B, H, Lq, Lk, sm_scale, seg, head, out=None, stream=None):
-    """INT32 accumulators and FP32 scores of one (segment, head): ([Lq, Lk] int32, [Lq, Lk] float32, O)."""
-    dev = quant.q.device
-    acc = torch.empty((Lq, Lk), dtype=torch.int32, device=dev)
-    s = torch.empty((Lq, Lk), dtype=torch.float32, device=dev)
-    if out is None:
-        out = torch.empty((B, Lq, H, D), dtype=torch.bfloat16, device=dev)
+def sattn_debug_scores(quant, sm_scale, seg, head, q_begin, q_end, q_step=1, Lq=None, Lk=None, ld=None, nep=0,
+                       cu_seqlens_q=None, cu_seqlens_k=None, out=None, scores=True, stream=None):
+    """Checkpoints of the sampled query rows q_begin, q_begin + q_step, ... < q_end of one
+    (segment, head).  Dense problems: Lq, Lk are the per-segment lengths (the segments are
+    quant.nseg); packed: cu_seqlens tensors, and Lq, Lk the packed totals (default: what
+    `quant` was sized for).  ld: keys per dumped score row (default Lk); nep: epochs of
+    per-epoch checkpoints (0: none).  Returns a dict of device tensors: acc and s
+    ([rows, ld], with scores=True), m, d, alpha ([rows, nep]), p8 ([rows, nep, 64]) and ro
+    ([rows, nep, 128]) when nep > 0, and out, the forward output (the sampled rows of
+    `head` only are written)."""
+    dev = quant.k.device
+    varlen = cu_seqlens_q is not None
+    if varlen:
+        Lq = quant.total_q if Lq is None else Lq
+        Lk = quant.total_k if Lk is None else Lk
+    ld = Lk if ld is None else ld
+    rows = max(0, -(-(q_end - q_begin) // q_step))
+    r = {}
+    with _on(stream):
+        if scores:
+            r["acc"] = torch.zeros((rows, ld), dtype=torch.int32, device=dev)
+            r["s"] = torch.zeros((rows, ld), dtype=torch.float32, device=dev)
+        if nep:
+            for n in ("m", "d", "alpha"):
+                r[n] = torch.zeros((rows, nep), dtype=torch.float32, device=dev)
+            r["p8"] = torch.zeros((rows, nep, 64), dtype=torch.uint8, device=dev)
+            r["ro"] = torch.zeros((rows, nep, D), dtype=torch.float32, device=dev)
+        if out is None:
+            shape = (Lq, quant.H, D) if varlen else (quant.nseg, Lq, quant.H, D)
+            out = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    r["out"] = out
+    ck = Checkpoints(_ptr(r.get("acc")), _ptr(r.get("s")), ld if scores else 0, _ptr(r.get("m")), _ptr(r.get("d")),
+                     _ptr(r.get("alpha")), _ptr(r.get("p8")), _ptr(r.get("ro")), nep)
     st = quant.struct()
-    _check(lib().sattn_debug_scores(ctypes.byref(st), B, H, Lq, Lk, D, float(sm_scale), seg, head, acc.data_ptr(),
-                                    s.data_ptr(), _view(out, BF16Out), _stream(stream)), "sattn_debug_scores")
-    return acc, s, out
+    _check(lib().sattn_debug_scores(ctypes.byref(st), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), quant.nseg, Lq, Lk,
+                                    quant.H, D, float(sm_scale), seg, head, q_begin, q_end, q_step, ctypes.byref(ck),
+                                    _view(out, BF16Out), _stream(stream)), "sattn_debug_scores")
+    return r
 
 
 # ---------------------------------------------------------------- layout inspection

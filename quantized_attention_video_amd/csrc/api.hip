@@ -153,8 +153,7 @@ static sattn_status fwd_common(const sattn_qkv_quant* qkv, int H, int D, float s
 static float log2e_scale(float sm_scale) { return (float)((double)sm_scale * 1.4426950408889634); }
 
 static sattn_status fwd_dense(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D, float sm_scale,
-                              sattn_bf16_out o, int dump_seg, int dump_head, int32_t* acc_out, float* s_out,
-                              void* stream) {
+                              sattn_bf16_out o, void* stream) {
   if (B < 1 || Lq < 0 || Lk < 0) return SATTN_EINVAL;
   sattn_status st = fwd_common(qkv, H, D, sm_scale, o, true);
   if (st != SATTN_OK) return st;
@@ -171,34 +170,77 @@ static sattn_status fwd_dense(const sattn_qkv_quant* qkv, int B, int H, int Lq, 
   p.c32 = log2e_scale(sm_scale);
   p.o = static_cast<uint16_t*>(o.ptr);
   p.o_st = o.stride_t; p.o_sh = o.stride_h;
-  p.dump_acc = acc_out; p.dump_s = s_out;
-  p.dump_seg = dump_seg; p.dump_head = dump_head; p.dump_lk = Lk;
   p.q_scale_shift = q_scale_shift(qkv);
   p.max_kblocks = ceil64(Lk);
   const int qpw = attn_queries_per_wg();
   const int64_t ntile = ceil64(Lq) * 64 / qpw + (ceil64(Lq) * 64 % qpw != 0);
   const int64_t grid = 8 * (int64_t)((H + 7) / 8) * B * ntile;
   if (grid > kMaxGroups256) return SATTN_EUNSUPPORTED;
-  return launch_attention(p, grid, acc_out != nullptr, static_cast<hipStream_t>(stream)) == hipSuccess
-             ? SATTN_OK
-             : SATTN_EHIP;
+  return launch_attention(p, grid, false, static_cast<hipStream_t>(stream)) == hipSuccess ? SATTN_OK : SATTN_EHIP;
 }
 
 sattn_status sattn_fwd(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D, float sm_scale,
                        sattn_bf16_out o, void* stream) {
-  return fwd_dense(qkv, B, H, Lq, Lk, D, sm_scale, o, -1, -1, nullptr, nullptr, stream);
+  return fwd_dense(qkv, B, H, Lq, Lk, D, sm_scale, o, stream);
 }
 
-sattn_status sattn_debug_scores(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D, float sm_scale,
-                                int seg, int head, int32_t* acc_out, float* s_out, sattn_bf16_out o, void* stream) {
-  if (acc_out == nullptr || s_out == nullptr || seg < 0 || seg >= B || head < 0 || head >= H) return SATTN_EINVAL;
-  return fwd_dense(qkv, B, H, Lq, Lk, D, sm_scale, o, seg, head, acc_out, s_out, stream);
+sattn_status sattn_debug_scores(const sattn_qkv_quant* qkv, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int nseg, int64_t Lq, int64_t Lk, int H, int D, float sm_scale, int seg, int head,
+                                int64_t q_begin, int64_t q_end, int64_t q_step, const sattn_checkpoints* ck,
+                                sattn_bf16_out o, void* stream) {
+  if (nseg < 1 || Lq < 0 || Lk < 0 || ck == nullptr) return SATTN_EINVAL;
+  const bool varlen = cu_seqlens_q != nullptr;
+  if ((cu_seqlens_k != nullptr) != varlen) return SATTN_EINVAL;
+  sattn_status st = fwd_common(qkv, H, D, sm_scale, o, !varlen);
+  if (st != SATTN_OK) return st;
+  if (seg < 0 || seg >= nseg || head < 0 || head >= H || q_begin < 0 || q_end <= q_begin || q_step < 1 ||
+      ck->ld < 0 || ck->nep < 0 || ((ck->acc || ck->s) && ck->ld < 1) ||
+      ((ck->m || ck->d || ck->alpha || ck->p8 || ck->ro) && ck->nep < 1))
+    return SATTN_EINVAL;
+  int64_t q_clip, k_clip;
+  if (varlen) {
+    if (qkv->qblk_cap < nseg || qkv->kblk_cap < nseg) return SATTN_ENOSPACE;
+    q_clip = Lq < clip_for_cap(qkv->qblk_cap, nseg) ? Lq : clip_for_cap(qkv->qblk_cap, nseg);
+    k_clip = Lk < clip_for_cap(qkv->kblk_cap, nseg) ? Lk : clip_for_cap(qkv->kblk_cap, nseg);
+  } else {
+    if (qkv->qblk_cap < (int64_t)nseg * ceil64(Lq) || qkv->kblk_cap < (int64_t)nseg * ceil64(Lk))
+      return SATTN_ENOSPACE;
+    q_clip = Lq;
+    k_clip = Lk;
+  }
+  if (q_end > q_clip) q_end = q_clip;  // no segment holds more queries than the view
+  if (q_end <= q_begin) return SATTN_OK;
+  AttnParams p;
+  memset(&p, 0, sizeof(p));
+  p.q8 = qkv->q; p.q_scale = qkv->q_scale;
+  p.k8 = qkv->k; p.k_scale = qkv->k_scale;
+  p.v8 = qkv->v; p.v_scale = qkv->v_scale;
+  p.qblk_cap = qkv->qblk_cap; p.kblk_cap = qkv->kblk_cap;
+  p.H = H; p.nseg = nseg;
+  p.gq = SegGeom{cu_seqlens_q, nseg, q_clip, varlen ? 0 : o.stride_b};
+  p.gk = SegGeom{cu_seqlens_k, nseg, k_clip, 0};
+  p.c32 = log2e_scale(sm_scale);
+  p.o = static_cast<uint16_t*>(o.ptr);
+  p.o_st = o.stride_t; p.o_sh = o.stride_h;
+  p.q_scale_shift = q_scale_shift(qkv);
+  p.max_kblocks = ceil64(k_clip);  // selects the K-scale path exactly as the forward does
+  DumpParams& d = p.dump;
+  d.acc = ck->acc; d.s = ck->s; d.ld = ck->ld;
+  d.m = ck->m; d.d = ck->d; d.alpha = ck->alpha; d.p8 = ck->p8; d.ro = ck->ro; d.nep = ck->nep;
+  d.seg = seg; d.head = head;
+  d.q0 = q_begin; d.q1 = q_end; d.qstep = q_step;
+  const int qpw = attn_queries_per_wg();
+  d.tile0 = q_begin / qpw;
+  const int64_t grid = (q_end - 1) / qpw - d.tile0 + 1;
+  if (grid > kMaxGroups256) return SATTN_EUNSUPPORTED;
+  return launch_attention(p, grid, true, static_cast<hipStream_t>(stream)) == hipSuccess ? SATTN_OK : SATTN_EHIP;
 }
 
 sattn_status sattn_fwd_varlen(const sattn_qkv_quant* qkv, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                              int nseg, int64_t total_q, int H, int D, float sm_scale, sattn_bf16_out o,
-                              void* workspace, size_t workspace_bytes, void* stream) {
-  if (nseg < 1 || total_q < 0 || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return SATTN_EINVAL;
+                              int nseg, int64_t total_q, int64_t total_k, int H, int D, float sm_scale,
+                              sattn_bf16_out o, void* workspace, size_t workspace_bytes, void* stream) {
+  if (nseg < 1 || total_q < 0 || total_k < 0 || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)
+    return SATTN_EINVAL;
   sattn_status st = fwd_common(qkv, H, D, sm_scale, o, false);
   if (st != SATTN_OK) return st;
   if (workspace == nullptr || !aligned16(workspace)) return SATTN_EINVAL;
@@ -207,7 +249,8 @@ sattn_status sattn_fwd_varlen(const sattn_qkv_quant* qkv, const int32_t* cu_seql
   int32_t* order = static_cast<int32_t*>(workspace);
   int32_t* tpref = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align_up((size_t)nseg * 4));
   const int64_t q_clip = total_q < clip_for_cap(qkv->qblk_cap, nseg) ? total_q : clip_for_cap(qkv->qblk_cap, nseg);
-  const int64_t k_clip = clip_for_cap(qkv->kblk_cap, nseg);
+  // the quantizer's clipping: keys past the K/V views' total_k tokens were never quantized
+  const int64_t k_clip = total_k < clip_for_cap(qkv->kblk_cap, nseg) ? total_k : clip_for_cap(qkv->kblk_cap, nseg);
   AttnParams p;
   memset(&p, 0, sizeof(p));
   p.q8 = qkv->q; p.q_scale = qkv->q_scale;
@@ -221,7 +264,6 @@ sattn_status sattn_fwd_varlen(const sattn_qkv_quant* qkv, const int32_t* cu_seql
   p.c32 = log2e_scale(sm_scale);
   p.o = static_cast<uint16_t*>(o.ptr);
   p.o_st = o.stride_t; p.o_sh = o.stride_h;
-  p.dump_seg = -1; p.dump_head = -1;
   p.q_scale_shift = q_scale_shift(qkv);
   p.max_kblocks = ceil64(k_clip);
   const int64_t tiles_bound = q_clip / attn_queries_per_wg() + nseg + 1;
@@ -258,7 +300,6 @@ sattn_status sattn_fwd_fused(const sattn_qkv_quant* kv, sattn_bf16_in q, const i
   p.c32 = log2e_scale(sm_scale);
   p.o = static_cast<uint16_t*>(o.ptr);
   p.o_st = o.stride_t; p.o_sh = o.stride_h;
-  p.dump_seg = -1; p.dump_head = -1;
   p.q_scale_shift = q_scale_shift(kv);
   p.max_kblocks = ceil64(k_clip);
   p.qbf = static_cast<const uint16_t*>(q.ptr);

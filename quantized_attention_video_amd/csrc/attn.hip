@@ -148,10 +148,17 @@ __device__ __forceinline__ void barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n
 // bookkeeping does not see an LDS-DMA write: it would otherwise make LDS reads that it
 // cannot prove disjoint wait for every outstanding tile request (vmcnt(0)).  Tile requests
 // are waited for explicitly and ordered against their readers by the workgroup barrier.
+// The instruction takes its LDS base from m0, a register the compiler reserves: the asm
+// saves m0, sets it, issues the load and restores it, so whatever the compiler keeps in
+// m0 is unchanged across the statement (two scalar moves per load).
 __device__ __forceinline__ void dma_chunk(const uint8_t* base, uint32_t lane_off, const uint8_t* lds) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(const lds_void_t*)lds;  // LDS byte address
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(base), "s"(m0)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(lane_off), "s"(base), "s"(m0)
+      : "memory");
 }
 
 struct Pipe {
@@ -169,12 +176,11 @@ struct Pipe {
   bool active;
 };
 
-// Checkpoint dump of the production score accumulators (sattn_debug_scores).
+// Checkpoint dump (sattn_debug_scores): the parameters, and this lane's sampled-row index
+// (-1 if its query row is not sampled).
 struct Dump {
-  int32_t* acc;
-  float* s;
-  int64_t lk, row, len_q;
-  bool on;
+  DumpParams p;
+  int64_t idx;
 };
 
 // A tile (8 KiB = 512 16-byte chunks) moves into an LDS slot; loader wave w, step j covers
@@ -184,6 +190,29 @@ __device__ __forceinline__ void issue_tile(const Pipe& c, const uint8_t* src_til
   const uint8_t* tile = src_tiles + (int64_t)e * kTileBytes;  // wave-uniform
 #pragma unroll
   for (int j = 0; j < kChunksPerTile; ++j) dma_chunk(tile, c.loff[j], slot + (j * kLoaderWaves + c.wave) * 1024);
+}
+
+// The steady steps' K tile and V tile in one statement: m0 saved once, set before each of the
+// four loads, restored once (the per-load save and restore of dma_chunk costs ~1.5 % of the
+// kernel's time when it runs in every step).
+__device__ __forceinline__ void issue_kv(const Pipe& c, const uint8_t* ktile, uint8_t* kdst, const uint8_t* vtile,
+                                         uint8_t* vdst) {
+  static_assert(kChunksPerTile == 2 && kLoaderWaves == kWaves, "two loads per lane and tile");
+  const uint32_t k0 = (uint32_t)(uintptr_t)(const lds_void_t*)(kdst + c.wave * 1024);
+  const uint32_t k1 = (uint32_t)(uintptr_t)(const lds_void_t*)(kdst + (kLoaderWaves + c.wave) * 1024);
+  const uint32_t v0 = (uint32_t)(uintptr_t)(const lds_void_t*)(vdst + c.wave * 1024);
+  const uint32_t v1 = (uint32_t)(uintptr_t)(const lds_void_t*)(vdst + (kLoaderWaves + c.wave) * 1024);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %3\n\t"
+      "s_mov_b32 m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %4\n\t"
+      "s_mov_b32 m0, %8\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %4\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(c.loff[0]), "v"(c.loff[1]), "s"(ktile), "s"(vtile), "s"(k0), "s"(k1), "s"(v0), "s"(v1)
+      : "memory");
 }
 
 // One S^T tile t of the first epoch: acc_t = K(keys 32t..32t+31) . Q^T over 128 channels,
@@ -298,6 +327,58 @@ __device__ __forceinline__ void rescale(Pipe& c) {
   }
 }
 
+// ---------------------------------------------------------------- checkpoint dump
+// The checkpoint quantities of the Phase 2B report's "Exactness" section for the sampled
+// query rows, written from the registers of this instantiation (the production kernel with
+// stores added): INT32 accumulators and FP32 scores per key, and per epoch the running max,
+// the denominator, the rescale factor, the E4M3 probability bytes and the running output.
+__device__ __forceinline__ void dump_scores(const Pipe& c, const Dump& dump, int e, int kvalid, const v16i (&acc)[2],
+                                            float sig) {
+  if (dump.idx < 0) return;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * t + 8 * (r >> 2) + 4 * c.g + (r & 3);
+      const int64_t j = (int64_t)e * kBlk + key;
+      if (key < kvalid && j < dump.p.ld) {
+        const int64_t o = dump.idx * dump.p.ld + j;
+        const int32_t a = acc[t][r] - kAccBias;
+        if (dump.p.acc) dump.p.acc[o] = a;
+        if (dump.p.s) dump.p.s[o] = (float)a * sig;  // fl32(acc * sigma)
+      }
+    }
+}
+
+// Epoch e's running max m, rescale factor alpha and denominator d (both half-waves' partial
+// sums, in units of 448 P), and its E4M3 probability bytes in key order.
+__device__ __forceinline__ void dump_epoch(const Pipe& c, const Dump& dump, int e, float alpha, const v8i& pb) {
+  const float dsum = xhalf_sum(c.dpart);  // cross-lane: every lane of the wave takes part
+  if (dump.idx < 0 || e >= dump.p.nep) return;
+  const int64_t o = dump.idx * dump.p.nep + e;
+  if (dump.p.m) dump.p.m[o] = c.m;
+  if (dump.p.alpha) dump.p.alpha[o] = alpha;
+  if (dump.p.d) dump.p.d[o] = dsum;
+  if (dump.p.p8) {
+    uint8_t* row = dump.p.p8 + o * kBlk;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r3 = 0; r3 < 4; ++r3)
+        row[32 * (j >> 2) + 8 * (j & 3) + 4 * c.g + r3] = (uint8_t)(((uint32_t)pb[j] >> (8 * r3)) & 0xffu);
+  }
+}
+
+// The running output RO after epoch e (this lane's 64 of the row's 128 channels).
+__device__ __forceinline__ void dump_ro(const Pipe& c, const Dump& dump, int e) {
+  if (dump.idx < 0 || e < 0 || e >= dump.p.nep || dump.p.ro == nullptr) return;
+  float* row = dump.p.ro + (dump.idx * dump.p.nep + e) * kD;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) row[32 * w + 8 * (i >> 2) + 4 * c.g + (i & 3)] = c.oacc[w][i];
+}
+
 // Pipeline step for epoch e (ST = e % kUnroll).  Its scores are already in acc (QK issued
 // during the previous step).  Wait until K(e+1) and V(e-1) have landed (the requests of
 // step e-1 may stay in flight), barrier, request K(e+3) and V(e+1), then rescale O by
@@ -317,33 +398,29 @@ __device__ __forceinline__ void pipe_step(Pipe& c, int e, int kvalid, const Dump
     else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kChunksPerTile) : "memory");
   }
   barrier();  // K(e+1), V(e-1) visible to every wave; every wave is done with step e-1
-  if (STEADY || e + 3 < c.nkb) issue_tile(c, c.kg, e + 3, kslot<KS>());  // slot of K(e), read in step e-1
-  if (STEADY || e + 1 < c.nkb) issue_tile(c, c.vg, e + 1, vslot<KN>());  // slot of V(e-2), read in step e-1
+  // K(e+3) into the slot of K(e) and V(e+1) into the slot of V(e-2), both read in step e-1
+  if constexpr (STEADY) {
+    issue_kv(c, c.kg + (int64_t)(e + 3) * kTileBytes, kslot<KS>(), c.vg + (int64_t)(e + 1) * kTileBytes, vslot<KN>());
+  } else {
+    if (e + 3 < c.nkb) issue_tile(c, c.kg, e + 3, kslot<KS>());
+    if (e + 1 < c.nkb) issue_tile(c, c.vg, e + 1, vslot<KN>());
+  }
   if (!c.active) return;
   rescale(c);  // O = RO(e-2) * alpha(e-1), so PV(e-1) below completes RO(e-1)
   const float sig = c.sig_q * c.ks_next;  // fl32(fl32(q_scale * c) * k_scale)
   if (STEADY || e + 1 < c.nkb) c.ks_next = KSL ? g_ks[e + 1] : c.ksc[e + 1];
-  if constexpr (DUMP) {
-    if (dump.on && dump.row < dump.len_q) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * t + 8 * (r >> 2) + 4 * c.g + (r & 3);
-          if (key < kvalid) {
-            const int64_t o = dump.row * dump.lk + (int64_t)e * kBlk + key;
-            dump.acc[o] = acc[t][r] - kAccBias;
-            dump.s[o] = (float)(acc[t][r] - kAccBias) * sig;
-          }
-        }
-    }
-  }
+  if constexpr (DUMP) dump_scores(c, dump, e, kvalid, acc, sig);
   c.alpha_prev = softmax_pv<TAIL, !LAST>(c, acc, sig, kvalid, c.pb[ST & 1], c.pb[(ST + 1) & 1], vslot<VP>(),
                                          kslot<KN>());
+  if constexpr (DUMP) {
+    dump_epoch(c, dump, e, c.alpha_prev, c.pb[ST & 1]);
+    dump_ro(c, dump, e - 1);  // the P.V of epoch e-1 has just been accumulated
+  }
   if constexpr (LAST) {
     rescale(c);
 #pragma unroll
     for (int w = 0; w < 4; ++w) pv_tile(c.oacc[w], vslot<KS>(), c.pb[ST & 1], c.lane, w);
+    if constexpr (DUMP) dump_ro(c, dump, e);
   }
 }
 
@@ -379,12 +456,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level addressing in SGPRs
 
   // ---------------------------------------------------------------- work item
+  int s, h;
+  int64_t qt;
+  if constexpr (DUMP) {  // the query tiles of one (segment, head) that hold sampled rows
+    s = p.dump.seg;
+    h = p.dump.head;
+    qt = p.dump.tile0 + blockIdx.x;
+  } else {
   const int xcd = blockIdx.x & 7;
   const int64_t kk = blockIdx.x >> 3;
   const int nh = xcd < p.H ? (p.H - xcd + 7) / 8 : 0;
   if (nh == 0) return;
-  int s;
-  int64_t hl, qt;
+  int64_t hl;
   if (p.order == nullptr) {
     const int64_t ntile = (ceil_blocks(p.gq.L) + kQBlocksPerWG - 1) / kQBlocksPerWG;
     const int64_t per_seg = (int64_t)nh * ntile;
@@ -406,13 +489,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     qt = rem - hl * ntile;
     s = p.order[lo];
   }
-  const int h = xcd + 8 * (int)hl;
+  h = xcd + 8 * (int)hl;
+  }
   const SegInfo qi = seg_info(p.gq, s, p.o_st);
   const SegInfo ki = seg_info(p.gk, s, 0);
   const int nkb = (int)ceil_blocks(ki.len);
   const int last_valid = (int)(ki.len - (int64_t)(nkb - 1) * kBlk);  // keys in the last epoch
   const int64_t qb = qt * kQBlocksPerWG + (wave >> 1);  // this wave's 64-query block
   const int hq = wave & 1;                              // and which 32 of its queries
+  if constexpr (DUMP) {  // no sampled row in this tile (uniform over the workgroup): done
+    const int64_t lo = max(qt * kQPerWG, p.dump.q0);
+    const int64_t hi = min(min(qt * kQPerWG + kQPerWG, p.dump.q1), qi.len);
+    const int64_t first = p.dump.q0 + (lo - p.dump.q0 + p.dump.qstep - 1) / p.dump.qstep * p.dump.qstep;
+    if (first >= hi) return;
+  }
 
 
   Pipe c;
@@ -488,12 +578,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   }
 
   Dump dump;
-  dump.acc = p.dump_acc;
-  dump.s = p.dump_s;
-  dump.lk = p.dump_lk;
-  dump.row = qb * kBlk + hq * 32 + (lane & 31);
-  dump.len_q = qi.len;
-  dump.on = DUMP && s == p.dump_seg && h == p.dump_head;
+  dump.idx = -1;
+  if constexpr (DUMP) {
+    dump.p = p.dump;
+    const int64_t row = qb * kBlk + hq * 32 + (lane & 31), off = row - p.dump.q0;
+    if (off >= 0 && row < p.dump.q1 && row < qi.len && off % p.dump.qstep == 0) dump.idx = off / p.dump.qstep;
+  }
 
   // ---------------------------------------------------------------- epoch pipeline
   // Step e reads K(e+1) and V(e-1).  Step 0's deferred PV multiplies the V slot of epoch
@@ -553,6 +643,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   const float inv = dtot > 0.f ? 1.0f / dtot : 0.f;
   const int64_t row = qb * kBlk + hq * 32 + (lane & 31);
   if (row >= qi.len) return;
+  if (DUMP && dump.idx < 0) return;  // the checkpoint run writes the sampled rows only
   uint16_t* orow = p.o + qi.elem_base + row * p.o_st + (int64_t)h * p.o_sh;
   const float* vsc = p.v_scale + ((int64_t)s * p.H + h) * kD;
 #pragma unroll
@@ -632,8 +723,10 @@ hipError_t launch_plan(const int32_t* cu_q, const int32_t* cu_k, int nseg, int64
 
 hipError_t launch_attention(const AttnParams& p, int64_t grid, bool dump, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  const bool ksl = p.max_kblocks <= kKsLds;
-  if (dump)  // the score dump is a debugging path: scales through the scalar cache
+  const bool ksl = p.max_kblocks <= kKsLds;  // the same K-scale path with and without the dump
+  if (dump && ksl)
+    hipLaunchKernelGGL((attn_fwd_kernel<true, true>), dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, p);
+  else if (dump)
     hipLaunchKernelGGL((attn_fwd_kernel<true, false>), dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, p);
   else if (ksl)
     hipLaunchKernelGGL((attn_fwd_kernel<false, true>), dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, p);

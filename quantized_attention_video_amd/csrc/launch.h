@@ -28,6 +28,21 @@ struct QuantLaunch {
   size_t ws_sums_bytes, ws_vmax_bytes;
 };
 
+// Checkpoint dump of one (segment, head) (sattn_debug_scores): sampled query rows
+// q0, q0 + qstep, ... < q1 of the segment; row i of every buffer is the i-th sampled row.
+struct DumpParams {
+  int32_t* acc;  // [rows][ld] INT32 accumulators
+  float* s;      // [rows][ld] FP32 scores
+  int64_t ld;
+  float *m, *d, *alpha;  // [rows][nep]
+  uint8_t* p8;           // [rows][nep][64]
+  float* ro;             // [rows][nep][128]
+  int64_t nep;
+  int seg, head;
+  int64_t q0, q1, qstep;
+  int64_t tile0;  // first query tile of the launch (workgroup b takes tile tile0 + b)
+};
+
 struct AttnParams {
   const int8_t* q8;
   const float* q_scale;
@@ -44,10 +59,7 @@ struct AttnParams {
   float c32;             // fl32(sm_scale * log2 e)
   uint16_t* o;
   int64_t o_st, o_sh;
-  int32_t* dump_acc;
-  float* dump_s;
-  int dump_seg, dump_head;
-  int64_t dump_lk;
+  DumpParams dump;       // used by the checkpoint instantiation only
   int64_t max_kblocks;  // bound on any segment's key blocks (selects the K-scale path)
   int q_scale_shift;    // Q scales per 64-token block: 1 << q_scale_shift (1 or 2)
   const uint16_t* qbf;  // BF16 Q view quantized in the kernel (sattn_fwd_fused), else nullptr

@@ -137,7 +137,7 @@ int run(const char* in_path, const char* out_path) {
                                           sz.quant_workspace_bytes, stream),
                        "sattn_quantize_qkv");
   if (good && packed)
-    good = sattn_ok(sattn_fwd_varlen(&quant, dcq, dck, nseg, tq, H, kD, sm_scale, o, fws, sz.fwd_workspace_bytes,
+    good = sattn_ok(sattn_fwd_varlen(&quant, dcq, dck, nseg, tq, tk, H, kD, sm_scale, o, fws, sz.fwd_workspace_bytes,
                                      stream),
                     "sattn_fwd_varlen");
   else if (good)

@@ -123,12 +123,47 @@ def test_fwd_validation():
     assert f(ctypes.byref(_quant_struct(cap=1 << 40)), 1, 8, (1 << 31) - 1, 64, 128, 0.1, _out(), None) \
         == B.SATTN_EUNSUPPORTED
     v = L.sattn_fwd_varlen
-    assert v(ctypes.byref(q), FAKE, FAKE, 2, 100, 1, 128, 0.1, _out(), FAKE, 4, None) == B.SATTN_ENOSPACE
-    assert v(ctypes.byref(q), None, FAKE, 2, 100, 1, 128, 0.1, _out(), FAKE, 1024, None) == B.SATTN_EINVAL
-    assert v(ctypes.byref(q), FAKE, FAKE, 2, 100, 1, 128, 0.1, _out(), None, 1024, None) == B.SATTN_EINVAL
+    assert v(ctypes.byref(q), FAKE, FAKE, 2, 100, 100, 1, 128, 0.1, _out(), FAKE, 4, None) == B.SATTN_ENOSPACE
+    assert v(ctypes.byref(q), None, FAKE, 2, 100, 100, 1, 128, 0.1, _out(), FAKE, 1024, None) == B.SATTN_EINVAL
+    assert v(ctypes.byref(q), FAKE, FAKE, 2, 100, 100, 1, 128, 0.1, _out(), None, 1024, None) == B.SATTN_EINVAL
+    assert v(ctypes.byref(q), FAKE, FAKE, 2, 100, -1, 1, 128, 0.1, _out(), FAKE, 1024, None) == B.SATTN_EINVAL
+
+
+def _ck(**kw):
+    c = dict(acc=FAKE, s=FAKE, ld=64, m=None, d=None, alpha=None, p8=None, ro=None, nep=0)
+    c.update(kw)
+    return B.Checkpoints(*(c[n] for n, _ in B.Checkpoints._fields_))
+
+
+def test_debug_scores_validation():
+    """Row range, step, segment/head indices and checkpoint buffers are checked before any
+    launch (dense and packed forms)."""
+    L = B.lib()
+    q = _quant_struct()
     d = L.sattn_debug_scores
-    assert d(ctypes.byref(q), 1, 1, 64, 64, 128, 0.1, 1, 0, FAKE, FAKE, _out(), None) == B.SATTN_EINVAL
-    assert d(ctypes.byref(q), 1, 1, 64, 64, 128, 0.1, 0, 0, None, FAKE, _out(), None) == B.SATTN_EINVAL
+
+    def call(cu=None, nseg=1, Lq=64, Lk=64, H=1, D=128, seg=0, head=0, q0=0, q1=64, step=1, ck=None, out=None):
+        ck = _ck() if ck is None else ck
+        return d(ctypes.byref(q), cu, cu, nseg, Lq, Lk, H, D, 0.1, seg, head, q0, q1, step, ctypes.byref(ck),
+                 out or _out(), None)
+
+    assert call(D=64) == B.SATTN_EUNSUPPORTED
+    assert call(seg=1) == B.SATTN_EINVAL
+    assert call(seg=-1) == B.SATTN_EINVAL
+    assert call(head=1) == B.SATTN_EINVAL
+    assert call(q0=-1) == B.SATTN_EINVAL
+    assert call(q0=10, q1=10) == B.SATTN_EINVAL
+    assert call(step=0) == B.SATTN_EINVAL
+    assert call(ck=_ck(ld=0)) == B.SATTN_EINVAL            # scores asked for without a row length
+    assert call(ck=_ck(m=FAKE, nep=0)) == B.SATTN_EINVAL   # per-epoch buffer without epochs
+    assert call(ck=_ck(p8=FAKE, nep=0)) == B.SATTN_EINVAL
+    assert call(ck=_ck(ro=FAKE, nep=-1)) == B.SATTN_EINVAL
+    assert call(out=_out(ptr=MISALIGNED)) == B.SATTN_EINVAL
+    assert d(ctypes.byref(q), None, None, 1, 64, 64, 1, 128, 0.1, 0, 0, 0, 64, 1, None, _out(), None) \
+        == B.SATTN_EINVAL
+    assert d(ctypes.byref(q), FAKE, None, 1, 64, 64, 1, 128, 0.1, 0, 0, 0, 64, 1, ctypes.byref(_ck()), _out(),
+             None) == B.SATTN_EINVAL  # one cu_seqlens pointer without the other
+    assert call(nseg=2, Lq=64, Lk=64 * 1000) == B.SATTN_ENOSPACE  # capacity of the quantized K buffers
 
 
 def test_untile_layouts_are_permutations():

@@ -30,12 +30,16 @@ def _say(*a):
 
 
 def _sample_rows(L, full_below=2100):
-    """All rows of short sequences; first, middle and last 64-row blocks of long ones."""
+    """All rows of short sequences; of long ones the first, middle and last 64-row blocks
+    plus one row of every 128-query tile, its position in the tile varying from tile to tile
+    (so that every wave and lane position of the attention workgroups is reached)."""
     if L <= full_below:
         return np.arange(L)
     mid = (L // 2) // 64 * 64
     last = (L - 1) // 64 * 64
-    return np.unique(np.concatenate([np.arange(0, 64), np.arange(mid, mid + 64), np.arange(last, L)]))
+    per_tile = np.arange(0, L, 128) + (np.arange(0, L, 128) // 128 * 37) % 128
+    return np.unique(np.concatenate([np.arange(0, 64), np.arange(mid, mid + 64), np.arange(last, L),
+                                     per_tile[per_tile < L]]))
 
 
 def _tensor_cu(cu):
@@ -110,20 +114,62 @@ def test_quantized_buffers_bit_exact(name):
     _assert_quantized_equal(c["quant"], c["oq"], _blocks(inp["cu_q"], w), _blocks(inp["cu_k"], w), w.H)
 
 
-@pytest.mark.parametrize("name,seg,head", [("fixed_q128_kv192", 0, 0), ("dense_h8_l4096", 0, 5),
-                                           ("ragged_b2_h16_l1000", 1, 9), ("ragged_b2_h16_l2049", 1, 3)])
-def test_scores_bit_exact(name, seg, head):
-    c = case(name)
-    w = c["w"]
-    Bn, Lq, H = c["inp"]["q"].shape[:3]
-    Lk = c["inp"]["k"].shape[1]
-    acc, s, out = B.sattn_debug_scores(c["quant"], Bn, H, Lq, Lk, w.sm_scale, seg, head)
+def debug_run(c, seg, head, q0, q1, step=1, nep=0):
+    """sattn_debug_scores for one (segment, head) of a cached case, as the case was run."""
+    w, inp, quant = c["w"], c["inp"], c["quant"]
+    if w.varlen:
+        cq, ck = _tensor_cu(inp["cu_q"]), _tensor_cu(inp["cu_k"])
+        lk = inp["cu_k"][seg + 1] - inp["cu_k"][seg]
+        r = B.sattn_debug_scores(quant, w.sm_scale, seg, head, q0, q1, step, ld=lk, nep=nep, cu_seqlens_q=cq,
+                                 cu_seqlens_k=ck)
+    else:
+        r = B.sattn_debug_scores(quant, w.sm_scale, seg, head, q0, q1, step, Lq=inp["q"].shape[1],
+                                 Lk=inp["k"].shape[1], nep=nep)
     torch.cuda.synchronize()
-    r_acc, r_s = O.scores(c["oq"][seg], head, w.sm_scale)
-    assert np.array_equal(acc.cpu().numpy().astype(np.int64), r_acc.astype(np.int64))
-    assert np.array_equal(s.cpu().numpy(), r_s.astype(np.float32))
-    # the dump run computes the same forward output as the plain run
-    assert torch.equal(out, c["out"])
+    return r
+
+
+def _seg_rows(c, seg):
+    cu = c["inp"]["cu_q"]
+    return cu[seg + 1] - cu[seg]
+
+
+def assert_scores_exact(c, seg, head, q0, q1, step):
+    """INT32 accumulators and FP32 scores of the sampled rows bit-exact against the oracle,
+    and the checkpoint run's output rows bit-identical to the forward's."""
+    w = c["w"]
+    rows = np.arange(q0, min(q1, _seg_rows(c, seg)), step)
+    r = debug_run(c, seg, head, q0, q1, step)
+    _say(f"[scores] {w.name} seg {seg} head {head}: {len(rows)} rows x {r['acc'].shape[1]} keys")
+    r_acc, r_s = O.scores(c["oq"][seg], head, w.sm_scale, rows)
+    acc, sc = r["acc"][:len(rows)].cpu().numpy(), r["s"][:len(rows)].cpu().numpy()
+    bad = np.argwhere(acc.astype(np.int64) != r_acc.astype(np.int64))
+    assert len(bad) == 0, f"INT32 accumulators differ at {len(bad)} (row, key) pairs, first {bad[:5].tolist()}"
+    bad = np.argwhere(sc != r_s.astype(np.float32))
+    assert len(bad) == 0, f"FP32 scores differ at {len(bad)} (row, key) pairs, first {bad[:5].tolist()}"
+    if w.varlen:
+        base = c["inp"]["cu_q"][seg]
+        got, ref = r["out"][base + rows, head], c["out"][base + rows, head]
+    else:
+        got, ref = r["out"][seg, rows, head], c["out"][seg, rows, head]
+    assert torch.equal(got, ref), "the checkpoint run's output rows differ from the forward's"
+
+
+# (workload, segment, head, first row, row step): all rows of the small shapes; one row of
+# every 128-query tile (the position in the tile moving by one from tile to tile) of the
+# long sequences, in the launch configuration the throughput benchmark times.
+SCORE_CASES = [("fixed_q128_kv192", 0, 0, 0, 1), ("dense_h8_l4096", 0, 5, 3, 13), ("ragged_b2_h16_l1000", 1, 9, 0, 1),
+               ("ragged_b2_h16_l2049", 1, 3, 0, 1), ("ragged_b2_h16_l2049", 0, 15, 5, 3),
+               ("h3_video_l37810", 0, 0, 0, 129), ("h3_video_l37810", 0, 17, 64, 129),
+               ("h3_video_l37810", 0, 31, 127, 129),
+               ("varlen_h24_4seg", 0, 0, 11, 129), ("varlen_h24_4seg", 0, 23, 100, 129),
+               ("varlen_h24_4seg", 1, 7, 0, 65), ("varlen_h24_4seg", 2, 12, 0, 7), ("varlen_h24_4seg", 3, 5, 0, 1),
+               ("varlen_h24_4seg", 3, 18, 0, 1)]
+
+
+@pytest.mark.parametrize("name,seg,head,q0,step", SCORE_CASES)
+def test_scores_bit_exact(name, seg, head, q0, step):
+    assert_scores_exact(case(name), seg, head, q0, _seg_rows(case(name), seg), step)
 
 
 def _check_output(got, ref, label):
@@ -134,14 +180,22 @@ def _check_output(got, ref, label):
         assert np.mean(err) <= MAE, f"{label} head {h}: mae {np.mean(err):.3e}"
 
 
+@functools.lru_cache(maxsize=4)
+def oracle_rows(name, q_scale_rows=64):
+    """The oracle's output on the sampled rows of every segment and head: (rows, ref)."""
+    c = case(name, q_scale_rows)
+    oq = c["oq"]
+    rows = {si: _sample_rows(seg["q8"].shape[0]) for si, seg in enumerate(oq)}
+    _say(f"[oracle] {name}: attention on {sum(len(r) for r in rows.values())} rows of each of {c['w'].H} heads")
+    return rows, O.attention(oq, c["w"].sm_scale, rows=rows)
+
+
 @pytest.mark.parametrize("name", NAMES)
 def test_output_within_tolerance(name):
     c = case(name)
-    w, oq, inp = c["w"], c["oq"], c["inp"]
+    w, inp = c["w"], c["inp"]
     out = c["out"].float().cpu()
-    rows = {si: _sample_rows(seg["q8"].shape[0]) for si, seg in enumerate(oq)}
-    _say(f"[oracle] {name}: attention on {sum(len(r) for r in rows.values())} rows per head")
-    ref = O.attention(oq, w.sm_scale, rows=rows)
+    rows, ref = oracle_rows(name)
     for si, (a, b) in enumerate(O.segments(inp["cu_q"])):
         if w.varlen:
             got = out[a:b].numpy()
@@ -162,8 +216,7 @@ def test_quantization_error_against_exact_attention(name):
     w, oq, inp = c["w"], c["oq"], c["inp"]
     q64, k64, v64 = (W.packed_float64(inp[n]) for n in "qkv")
     out = c["out"].float().cpu().numpy().astype(np.float64)
-    rows = {si: _sample_rows(seg["q8"].shape[0]) for si, seg in enumerate(oq)}
-    ref = O.attention(oq, w.sm_scale, rows=rows)
+    rows, ref = oracle_rows(name)
     d_ex = d_or = n_ex = 0.0
     for si, ((a, b), (ka, kb)) in enumerate(zip(O.segments(inp["cu_q"]), O.segments(inp["cu_k"]))):
         if b == a or kb == ka:
@@ -208,35 +261,20 @@ def test_q32_quantized_buffers_bit_exact(name):
             assert np.array_equal(ks[h, bk[si]:bk[si] + nk], seg["k_scale"][h].astype(np.float32))
 
 
-@pytest.mark.parametrize("name", NAMES)
-def test_quantized_buffers_bit_exact(name):
-    c = case(name)
-    w, inp = c["w"], c["inp"]
-    _assert_quantized_equal(c["quant"], c["oq"], _blocks(inp["cu_q"], w), _blocks(inp["cu_k"], w), w.H)
-
-
-@pytest.mark.parametrize("name,seg,head", [("fixed_q128_kv192", 0, 0), ("ragged_b2_h16_l1000", 1, 9),
-                                           ("ragged_b2_h16_l2049", 0, 3)])
-def test_q32_scores_bit_exact(name, seg, head):
+@pytest.mark.parametrize("name,seg,head,q0,step", [("fixed_q128_kv192", 0, 0, 0, 1), ("ragged_b2_h16_l1000", 1, 9, 0, 1),
+                                                   ("ragged_b2_h16_l2049", 0, 3, 0, 1), ("varlen_h24_4seg", 0, 3, 31, 129),
+                                                   ("varlen_h24_4seg", 2, 20, 0, 5)])
+def test_q32_scores_bit_exact(name, seg, head, q0, step):
     c = case(name, 32)
-    w = c["w"]
-    Bn, Lq, H = c["inp"]["q"].shape[:3]
-    Lk = c["inp"]["k"].shape[1]
-    acc, s, out = B.sattn_debug_scores(c["quant"], Bn, H, Lq, Lk, w.sm_scale, seg, head)
-    torch.cuda.synchronize()
-    r_acc, r_s = O.scores(c["oq"][seg], head, w.sm_scale)
-    assert np.array_equal(acc.cpu().numpy().astype(np.int64), r_acc.astype(np.int64))
-    assert np.array_equal(s.cpu().numpy(), r_s.astype(np.float32))
-    assert torch.equal(out, c["out"])
+    assert_scores_exact(c, seg, head, q0, _seg_rows(c, seg), step)
 
 
 @pytest.mark.parametrize("name", Q32_NAMES)
 def test_q32_output_within_tolerance(name):
     c = case(name, 32)
-    w, oq, inp = c["w"], c["oq"], c["inp"]
+    w, inp = c["w"], c["inp"]
     out = c["out"].float().cpu()
-    rows = {si: _sample_rows(seg["q8"].shape[0]) for si, seg in enumerate(oq)}
-    ref = O.attention(oq, w.sm_scale, rows=rows)
+    rows, ref = oracle_rows(name, 32)
     for si, (a, b) in enumerate(O.segments(inp["cu_q"])):
         got = out[a:b].numpy() if w.varlen else out[si].numpy()
         _check_output(got[rows[si]].astype(np.float64), ref[si], f"{name} (32-row Q scales) seg {si}")
@@ -338,11 +376,11 @@ def test_k_mean_shift_changes_nothing_on_the_gpu():
     nb = L // 64  # the blocks written (the buffers hold one more of capacity, never written)
     assert torch.equal(qb.k[:, :nb], qa.k[:, :nb]) and torch.equal(qb.k_scale[:, :nb], qa.k_scale[:, :nb])
     for h in range(H):
-        acc_a, s_a, out_a = B.sattn_debug_scores(qa, 1, H, L, L, 0.0884, 0, h)
-        acc_b, s_b, out_b = B.sattn_debug_scores(qb, 1, H, L, L, 0.0884, 0, h)
+        ra = B.sattn_debug_scores(qa, 0.0884, 0, h, 0, L, Lq=L, Lk=L)
+        rb = B.sattn_debug_scores(qb, 0.0884, 0, h, 0, L, Lq=L, Lk=L)
         torch.cuda.synchronize()
-        assert torch.equal(acc_a, acc_b) and torch.equal(s_a, s_b)
-        assert torch.equal(out_a[:, :, h], out_b[:, :, h])
+        assert torch.equal(ra["acc"], rb["acc"]) and torch.equal(ra["s"], rb["s"])
+        assert torch.equal(ra["out"][:, :, h], rb["out"][:, :, h])
 
 
 def test_two_streams_at_once_match_one_after_the_other():
@@ -643,9 +681,123 @@ def test_large_shape_sampled_heads():
         assert np.array_equal(got_v, seg["v8"][:, j, :].astype(np.uint8)), f"v8 head {h}"
         assert np.array_equal(qs[h, :nblk].cpu().numpy(), seg["q_scale"][j].astype(np.float32)), f"q_scale {h}"
         assert np.array_equal(ks[h, :nblk].cpu().numpy(), seg["k_scale"][j].astype(np.float32)), f"k_scale {h}"
+    # one score row in about every second 128-query tile of head 29, bit-exact
+    srows = np.arange(3, w.Lq, 257)
+    r = B.sattn_debug_scores(quant, w.sm_scale, 0, 29, 3, w.Lq, 257, Lq=w.Lq, Lk=w.Lk)
+    torch.cuda.synchronize()
+    r_acc, r_s = O.scores(seg, heads.index(29), w.sm_scale, srows)
+    assert np.array_equal(r["acc"].cpu().numpy().astype(np.int64), r_acc.astype(np.int64)), "INT32 scores, head 29"
+    assert np.array_equal(r["s"].cpu().numpy(), r_s.astype(np.float32)), "FP32 scores, head 29"
+    assert torch.equal(r["out"][0, srows, 29], out[0, srows, 29])
     rows = _sample_rows(w.Lq)
     ref = O.attention(oq, w.sm_scale, rows={0: rows})[0]
     got = out[0][rows][:, heads].float().cpu().numpy().astype(np.float64)
     _check_output(got, ref, w.name)
     assert torch.isfinite(out.float()).all()
 
+
+
+# ---------------------------------------------------------------- per-epoch checkpoints
+EPS_MFMA = 2.0 ** -11  # error of one FP8 matrix instruction, relative to the magnitudes it adds
+def _ulp32(x):
+    """Spacing of binary32 values at |x| (elementwise, FP64)."""
+    x = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(x)) - 23)
+
+
+def _e4m3_midpoint_distance(x):
+    """Relative distance of x > 0 from the nearest rounding midpoint of the E4M3 grid
+    (4 significant bits, subnormal spacing 2^-9)."""
+    x = np.asarray(x, dtype=np.float64)
+    step = np.where(x >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(x, 2.0 ** -6))) - 3), 2.0 ** -9)
+    mid = (np.floor(x / step) + 0.5) * step
+    return np.abs(x - mid) / np.maximum(x, 1e-300)
+
+
+@pytest.mark.parametrize("name,seg,head,q0,step", [("fixed_q128_kv192", 0, 0, 0, 1), ("ragged_b2_h16_l1000", 1, 4, 2, 7),
+                                                   ("ragged_b2_h16_l2049", 0, 11, 0, 13), ("varlen_h24_4seg", 3, 9, 0, 1)])
+def test_epoch_checkpoints_against_the_oracle(name, seg, head, q0, step):
+    """The per-epoch checkpoints of the Phase 2B report's "Exactness" list, from the forward
+    kernel's own registers, against the oracle's recurrence on the same rows:
+      * running max m: exact (both are maxima of the same binary32 scores);
+      * rescale factor alpha: 0 on the first epoch, 1 where m did not change, else within the
+        error of the hardware exp2 of fl32(m - m') (2^-22 relative + the argument's rounding);
+      * E4M3 probability bytes: identical, except where the FP64 448 P lies within the GPU's
+        bound on its exponent-argument error of an E4M3 rounding midpoint (each such key is
+        printed with its distance);
+      * denominator (units of 448 P): within a bound derived from the FP32 partial sums;
+      * running output RO: within a bound built from the per-instruction precision of the
+        FP8 matrix instruction (E4M3 products are exact, but the instruction adds its 64
+        products and the accumulator with less than FP32 precision: about 2^-14 of the sum
+        of their magnitudes on gfx950, measured; the bound allows 2^-11), the rescale and
+        the flipped bytes.
+    The hardware exp2 is not correctly rounded, so alpha, d and RO cannot be compared bit
+    for bit."""
+    c = case(name)
+    w = c["w"]
+    oseg = c["oq"][seg]
+    L = _seg_rows(c, seg)
+    Lk = oseg["k8"].shape[0]
+    nep = -(-Lk // 64)
+    rows = np.arange(q0, L, step)
+    r = debug_run(c, seg, head, q0, L, step, nep=nep)
+    g = {k: v[:len(rows)].cpu().numpy() for k, v in r.items() if k != "out"}
+    _, S = O.scores(oseg, head, w.sm_scale, rows)
+    vv = oseg["v8val"][:, head, :]
+    cps = []
+    O.online_softmax_pv(S, vv, checkpoints=cps)
+    log2_448 = float(np.float32(np.log2(448.0)))
+    flips = 0
+    ro_bound = np.zeros((len(rows), 128))  # bound on |RO_gpu - RO_oracle| after the epoch
+    d_rel = 0.0                            # accumulated relative error of the rescale factors in d
+    for e, cp in enumerate(cps):
+        m, alpha, p8, ro = cp["m"], cp["alpha"], cp["p"], cp["RO"]
+        k0, k1 = 64 * e, min(64 * e + 64, Lk)
+        assert np.array_equal(g["m"][:, e], m.astype(np.float32)), f"m, epoch {e}"
+        ga = g["alpha"][:, e].astype(np.float64)
+        if e == 0:
+            assert np.all(ga == 0)
+            eps_a = np.zeros(len(rows))
+        else:
+            prev = cps[e - 1]["m"]
+            same = prev == m
+            assert np.all(ga[same] == 1.0), f"alpha != 1 where m did not change, epoch {e}"
+            eps_a = np.where(same, 0.0, 2.0 ** -22 + np.log(2) * _ulp32(prev - m) / 2)
+            assert np.all(np.abs(ga - alpha) <= alpha * eps_a), f"alpha, epoch {e}"
+        # the GPU's exponent argument fl32(acc*sigma - fl32(m' - log2 448)) against the exact
+        # S - m' + log2 448: the roundings of S, of m' - log2 448 (with the binary32 log2 448)
+        # and of the argument, then the hardware exp2 (2^-22 relative)
+        Se = S[:, k0:k1]
+        mm = (m - log2_448).astype(np.float32).astype(np.float64)
+        arg = Se - m[:, None] + np.log2(448.0)
+        eps = np.log(2) * (_ulp32(Se) + _ulp32(mm)[:, None] + _ulp32(arg) + 2.0 ** -20) / 2 + 2.0 ** -22
+        p448 = 448.0 * np.exp2(Se - m[:, None])
+        ref_b = O.e4m3_encode(p8)
+        got_b = g["p8"][:, e, :k1 - k0]
+        diff = np.argwhere(got_b != ref_b)
+        for i, j in diff:
+            dist = _e4m3_midpoint_distance(p448[i, j])
+            _say(f"[p8] {name} epoch {e} row {rows[i]} key {k0 + j}: 448P = {p448[i, j]:.9g}, "
+                 f"{dist:.2e} from a rounding midpoint (bound {eps[i, j]:.2e}), bytes {got_b[i, j]} vs {ref_b[i, j]}")
+            assert dist <= eps[i, j], "an E4M3 byte differs away from a rounding midpoint"
+            assert abs(int(got_b[i, j]) - int(ref_b[i, j])) == 1, "a flip moves by more than one E4M3 step"
+        flips += len(diff)
+        # d in units of 448 P: each term within eps; FP32 partial sums of 8, then 4 and 2, the
+        # rescale and the two half-waves (about 14 roundings per epoch); the rescale factors' errors
+        d_rel = d_rel + float(np.max(eps_a))
+        dref = 448.0 * cp["d"]
+        tol_d = dref * (float(np.max(eps)) + d_rel + 14 * (e + 1) * 2.0 ** -24)
+        assert np.all(np.abs(g["d"][:, e] - dref) <= tol_d), f"d, epoch {e}"
+        # RO: the previous error rescaled, the rescale's rounding and alpha's error on the
+        # previous RO, one matrix instruction's error on its accumulator and 64 exact products
+        # (EPS_MFMA of their magnitudes), and the bytes that flipped
+        gp = O.e4m3_decode(got_b)
+        prev_ro = cps[e - 1]["RO"] if e else np.zeros_like(ro)
+        terms = (np.abs(prev_ro) + ro_bound) * alpha[:, None] + np.abs(p8) @ np.abs(vv[k0:k1])
+        ro_bound = (ro_bound * alpha[:, None] * (1 + eps_a[:, None]) + np.abs(prev_ro) * alpha[:, None] *
+                    (eps_a[:, None] + 2.0 ** -24) + EPS_MFMA * terms + np.abs(gp - p8) @ np.abs(vv[k0:k1]))
+        err = np.abs(g["ro"][:, e, :] - ro)
+        assert np.all(err <= ro_bound * 1.001 + 1e-30), f"RO, epoch {e}: max excess {np.max(err - ro_bound):.3e}"
+    _say(f"[checkpoints] {name} seg {seg} head {head}: {len(rows)} rows x {nep} epochs, {flips} E4M3 bytes at "
+         f"rounding midpoints")
+    assert flips <= max(2, 1e-4 * len(rows) * Lk), "too many probability bytes differ"

@@ -20,7 +20,7 @@ MAX_REL, MAE = 1e-2, 1e-3
 def _problem(seed):
     rng = np.random.default_rng(seed)
     g = torch.Generator().manual_seed(seed)
-    H = int(rng.choice([1, 2, 3, 5]))
+    H = int(rng.choice([1, 2, 3, 5, 9, 12, 20]))  # 9..23 heads: unequal heads per XCD (8 XCDs)
     rows = 32 if seed % 2 else 64
     varlen = bool(rng.integers(0, 2))
     if varlen:
@@ -61,7 +61,7 @@ def _to_cuda(t):
     return base.as_strided(t.shape, t.stride(), t.storage_offset())
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(20))
 def test_random_problem(seed):
     assert torch.cuda.is_available(), "GPU tests need an MI355X"
     p = _problem(1000 + seed)
