@@ -259,6 +259,28 @@ SATTN_API sattn_status sattn_fwd_fused(const sattn_qkv_quant* kv, sattn_bf16_in 
                              float sm_scale, sattn_bf16_out o, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/*
+ * sattn_quantize_qkv_noalloc — sattn_quantize_qkv for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops that allocate nothing, harnesses
+ * that forbid hipMalloc): the same arguments minus the workspace, the same results bit for
+ * bit.  Its workspace is a device array inside the library of sattn_noalloc_scratch_bytes()
+ * bytes (16 MiB), one per GPU, held until the process ends; the call makes no allocation.
+ * It uses the array of the device current on the calling thread, which must be the device
+ * of `stream` and of every buffer.  Returns SATTN_ENOSPACE when the problem's workspace
+ * (quant_workspace_bytes of sattn_quant_query) exceeds the array (beyond about 8,000
+ * segment-heads), SATTN_EUNSUPPORTED for a device index of 64 or more, and otherwise what
+ * sattn_quantize_qkv returns.  Every call on one GPU uses that GPU's one array: calls that
+ * overlap in time on one GPU (on different streams, or from different threads without
+ * ordering) race and give undefined results.  The array holds only intermediate sums that
+ * each call writes before it reads them, so no clearing is needed between calls.
+ */
+SATTN_API sattn_status sattn_quantize_qkv_noalloc(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in v, int nseg, int H,
+                                        int D, int64_t Lq, int64_t Lk, const int32_t* cu_seqlens_q,
+                                        const int32_t* cu_seqlens_k, const sattn_qkv_quant* out, void* stream);
+
+/* Size in bytes of the per-device workspace array of sattn_quantize_qkv_noalloc. */
+SATTN_API size_t sattn_noalloc_scratch_bytes(void);
+
 /* Static, human-readable name of a status code. */
 SATTN_API const char* sattn_status_string(sattn_status s);
 

@@ -17,7 +17,7 @@ D = 128
 
 SATTN_OK, SATTN_EINVAL, SATTN_EUNSUPPORTED, SATTN_ENOSPACE, SATTN_EHIP = range(5)
 EXPORTED = ("sattn_quant_query", "sattn_quantize_qkv", "sattn_fwd", "sattn_fwd_varlen", "sattn_debug_scores",
-            "sattn_fwd_fused", "sattn_status_string")
+            "sattn_fwd_fused", "sattn_quantize_qkv_noalloc", "sattn_noalloc_scratch_bytes", "sattn_status_string")
 
 
 class SattnError(RuntimeError):
@@ -77,10 +77,14 @@ def lib():
                                          i64, i64, ctypes.POINTER(Checkpoints), BF16Out, vp]
         L.sattn_fwd_fused.argtypes = [ctypes.POINTER(QKVQuant), BF16In, vp, vp, i32, i32, i64, i64, i32, f32,
                                       BF16Out, vp, ctypes.c_size_t, vp]
+        L.sattn_quantize_qkv_noalloc.argtypes = [BF16In, BF16In, BF16In, i32, i32, i32, i64, i64, vp, vp,
+                                                 ctypes.POINTER(QKVQuant), vp]
+        L.sattn_noalloc_scratch_bytes.argtypes = []
+        L.sattn_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.sattn_status_string.argtypes = [i32]
         L.sattn_status_string.restype = ctypes.c_char_p
         for name in EXPORTED:
-            if name != "sattn_status_string":
+            if name not in ("sattn_status_string", "sattn_noalloc_scratch_bytes"):
                 getattr(L, name).restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -199,6 +203,26 @@ def _on(stream):
     """Allocate temporaries on the stream the library call runs on (the caching allocator
     then never hands their memory to other work while that stream still uses it)."""
     return torch.cuda.stream(stream or torch.cuda.current_stream())
+
+
+def sattn_quantize_qkv_noalloc(q, k, v, out, cu_seqlens_q=None, cu_seqlens_k=None, stream=None):
+    """sattn_quantize_qkv into caller-allocated buffers `out` (from alloc_quantized), with the
+    library's per-device scratch array as its workspace: the call itself allocates nothing."""
+    varlen = cu_seqlens_q is not None
+    if varlen:
+        nseg, H, Lq, Lk = cu_seqlens_q.numel() - 1, q.shape[1], q.shape[0], k.shape[0]
+    else:
+        nseg, Lq, H, Lk = q.shape[0], q.shape[1], q.shape[2], k.shape[1]
+    st = out.struct()
+    qv = _view(q, BF16In) if out.q is not None else BF16In(0, 0, 0, 0)
+    _check(lib().sattn_quantize_qkv_noalloc(qv, _view(k, BF16In), _view(v, BF16In), nseg, H, D, Lq, Lk,
+                                            _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), ctypes.byref(st),
+                                            _stream(stream)), "sattn_quantize_qkv_noalloc")
+    return out
+
+
+def sattn_noalloc_scratch_bytes():
+    return int(lib().sattn_noalloc_scratch_bytes())
 
 
 def sattn_fwd(quant, B, H, Lq, Lk, sm_scale, out=None, stream=None):

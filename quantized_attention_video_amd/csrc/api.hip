@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "launch.h"
 #include "sattn.h"
 
@@ -58,6 +60,30 @@ constexpr int64_t kMaxGroups256 = 0xffffffffLL / 256;
 // Largest token count whose blocks fit a capacity (cap = floor(T/64) + nseg).
 int64_t clip_for_cap(int64_t cap, int nseg) { return cap >= nseg ? (cap - nseg) * 64 + 63 : 0; }
 
+// Quantizer workspace of sattn_quantize_qkv_noalloc: a file-scope device array, one copy on
+// every GPU the library runs on, held until the process ends.  Host code never uses the
+// name itself (on the host it is only a stand-in for the symbol): its device address is
+// looked up once per device, with that device current, and kept in scratch_ptr.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+sattn_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SATTN_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return SATTN_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SATTN_EHIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return SATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -91,9 +117,12 @@ sattn_status sattn_quant_query(int nseg, int64_t total_q, int64_t total_k, int H
   return SATTN_OK;
 }
 
-sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in v, int nseg, int H, int D, int64_t Lq,
-                                int64_t Lk, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                                const sattn_qkv_quant* out, void* workspace, size_t workspace_bytes, void* stream) {
+// sattn_quantize_qkv; with workspace == nullptr the device's scratch array is used instead
+// (sattn_quantize_qkv_noalloc), after every other argument has been validated.
+static sattn_status quantize_impl(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in v, int nseg, int H, int D, int64_t Lq,
+                                  int64_t Lk, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                  const sattn_qkv_quant* out, void* workspace, size_t workspace_bytes, bool use_scratch,
+                                  void* stream) {
   if (nseg < 1 || H < 1 || Lq < 0 || Lk < 0) return SATTN_EINVAL;
   if (D != kD || nseg > 65535 || H > 65535) return SATTN_EUNSUPPORTED;  // grid y/z extents
   const bool varlen = cu_seqlens_q != nullptr;
@@ -104,11 +133,13 @@ sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in 
       !view_ok(k.ptr, k.stride_b, k.stride_t, k.stride_h, !varlen) ||
       !view_ok(v.ptr, v.stride_b, v.stride_t, v.stride_h, !varlen))
     return SATTN_EINVAL;
-  if (!quant_bufs_ok(out, do_q) || workspace == nullptr || !aligned16(workspace)) return SATTN_EINVAL;
+  if (!quant_bufs_ok(out, do_q) || (!use_scratch && (workspace == nullptr || !aligned16(workspace))))
+    return SATTN_EINVAL;
   const int64_t total_q = varlen ? Lq : (int64_t)nseg * Lq;
   const int64_t total_k = varlen ? Lk : (int64_t)nseg * Lk;
   if ((do_q && out->qblk_cap < total_q / 64 + nseg) || out->kblk_cap < total_k / 64 + nseg) return SATTN_ENOSPACE;
   const QuantWs ws = quant_ws(nseg, H);
+  if (use_scratch) workspace_bytes = kScratchBytes;
   if (workspace_bytes < ws.total) return SATTN_ENOSPACE;
 
   QuantLaunch a;
@@ -137,8 +168,27 @@ sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in 
   if (a.q_blocks > kMaxGroups256 || a.k_blocks > kMaxGroups256 ||
       (int64_t)stats_chunks(nseg, H) * nseg * H + a.q_blocks * H > kMaxGroups256)
     return SATTN_EUNSUPPORTED;
+  if (use_scratch) {
+    const sattn_status st = scratch_for_current_device(&a.workspace);
+    if (st != SATTN_OK) return st;
+  }
   return launch_quantize(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SATTN_OK : SATTN_EHIP;
 }
+
+sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in v, int nseg, int H, int D, int64_t Lq,
+                                int64_t Lk, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                const sattn_qkv_quant* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return quantize_impl(q, k, v, nseg, H, D, Lq, Lk, cu_seqlens_q, cu_seqlens_k, out, workspace, workspace_bytes, false,
+                       stream);
+}
+
+sattn_status sattn_quantize_qkv_noalloc(sattn_bf16_in q, sattn_bf16_in k, sattn_bf16_in v, int nseg, int H, int D,
+                                        int64_t Lq, int64_t Lk, const int32_t* cu_seqlens_q,
+                                        const int32_t* cu_seqlens_k, const sattn_qkv_quant* out, void* stream) {
+  return quantize_impl(q, k, v, nseg, H, D, Lq, Lk, cu_seqlens_q, cu_seqlens_k, out, nullptr, 0, true, stream);
+}
+
+size_t sattn_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 static sattn_status fwd_common(const sattn_qkv_quant* qkv, int H, int D, float sm_scale, sattn_bf16_out o,
                                bool dense, bool need_q = true) {

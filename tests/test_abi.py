@@ -129,6 +129,28 @@ def test_fwd_validation():
     assert v(ctypes.byref(q), FAKE, FAKE, 2, 100, -1, 1, 128, 0.1, _out(), FAKE, 1024, None) == B.SATTN_EINVAL
 
 
+def test_noalloc_validation():
+    """The allocation-free quantizer validates like the workspace form, and rejects a problem
+    whose workspace exceeds its scratch array before any device call."""
+    L = B.lib()
+    assert L.sattn_noalloc_scratch_bytes() == 16 << 20
+    f = L.sattn_quantize_qkv_noalloc
+
+    def call(nseg=1, H=1, Lq=64, Lk=64, cu=None, out=None, D=128):
+        out = _quant_struct() if out is None else out
+        return f(_in(), _in(), _in(), nseg, H, D, Lq, Lk, cu, cu, ctypes.byref(out), None)
+
+    assert call(D=64) == B.SATTN_EUNSUPPORTED
+    assert call(nseg=0) == B.SATTN_EINVAL
+    assert call(Lk=-1) == B.SATTN_EINVAL
+    assert call(out=_quant_struct(rows=16)) == B.SATTN_EINVAL
+    assert call(out=_quant_struct(cap=1)) == B.SATTN_ENOSPACE
+    n = 9000  # segment-heads whose statistics (2 KiB each) exceed the 16 MiB array
+    assert call(nseg=n, Lq=n, Lk=n, cu=FAKE, out=_quant_struct(cap=1 << 20)) == B.SATTN_ENOSPACE
+    s = B.sattn_quant_query(n, n, n, 1)
+    assert s.quant_workspace_bytes > L.sattn_noalloc_scratch_bytes()
+
+
 def _ck(**kw):
     c = dict(acc=FAKE, s=FAKE, ld=64, m=None, d=None, alpha=None, p8=None, ro=None, nep=0)
     c.update(kw)
