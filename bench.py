@@ -17,7 +17,9 @@ INT8/FP8 MFMA peak, is the roofline entry.  The CPU baseline times the FP64 orac
 bounded sample of the same workload and extrapolates linearly.
 
 --latency (for the small shapes, e.g. --workload fixed_q128_kv192) reports the per-launch
-time of sattn_fwd the way the pages time their fixed-shape kernel: samples of 20
+time of sattn_fwd (given its forward workspace, so that grids too small for the GPU split
+each query tile's keys between two workgroups; --no-split withholds it) the way the pages
+time their fixed-shape kernel: samples of 20
 back-to-back launches, the per-launch time being a sample's event interval over 20; the
 launches are replayed from a captured HIP graph so that host enqueue time (Python and
 ctypes) does not stretch the interval, with the eager figure beside it.  Its CPU baseline
@@ -213,9 +215,10 @@ def latency(args, w, torch, B):
     out = torch.empty((Bn, Lq, H, 128), dtype=torch.bfloat16, device="cuda")
     B.sattn_quantize_qkv(q, k, v, out=quant)
     per = 20
+    ws = None if args.no_split else B.split_workspace(Bn, H, Lq, Lk)  # lets small grids split their keys
 
     def fwd():
-        B.sattn_fwd(quant, Bn, H, Lq, Lk, w.sm_scale, out=out)
+        B.sattn_fwd(quant, Bn, H, Lq, Lk, w.sm_scale, out=out, workspace=ws)
 
     fwd()
     torch.cuda.synchronize()
@@ -271,7 +274,7 @@ def latency(args, w, torch, B):
         "dtype": "int8 (QK) + fp8 e4m3 (PV), fp32 softmax",
         "data": _data_recipe(w),
         "config": {"workload": w.name, "B": Bn, "H": H, "Lq": Lq, "Lk": Lk, "D": 128, "layout": w.layout,
-                   "launches_per_sample": per},
+                   "launches_per_sample": per, "forward_workspace": ws is not None},
         "graph_replay_us": stats(graph),
         "eager_us": stats(eager),
         "single_launch_us": stats(single),
@@ -342,6 +345,8 @@ def main():
     ap.add_argument("--latency", action="store_true",
                     help="per-launch time of sattn_fwd on a small dense shape (samples of 20 launches)")
     ap.add_argument("--samples", type=int, default=500, help="--latency: samples of 20 launches")
+    ap.add_argument("--no-split", action="store_true",
+                    help="--latency: no forward workspace (small grids do not split their keys)")
     ap.add_argument("--copy-calib", type=int, default=0,
                     help="only run N plain 1 GiB device copies (counter calibration) and exit")
     ap.add_argument("--summarize-trace", metavar="CSV", help="print launch statistics of a rocprofv3 kernel trace")

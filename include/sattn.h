@@ -117,7 +117,7 @@ typedef struct {
   size_t q_bytes, q_scale_bytes, k_bytes, k_scale_bytes, k_mean_bytes, v_bytes, v_scale_bytes;
                                 /* q_scale_bytes holds either Q scale granularity     */
   size_t quant_workspace_bytes; /* workspace of sattn_quantize_qkv                     */
-  size_t fwd_workspace_bytes;   /* workspace of sattn_fwd_varlen (0 is enough for dense) */
+  size_t fwd_workspace_bytes;   /* workspace of sattn_fwd_varlen, and of sattn_fwd's key split */
 } sattn_sizes;
 
 /*
@@ -168,6 +168,15 @@ SATTN_API sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, satt
  * "Attention forward" / prequantized mainloop, and the checkpoint list of the
  * Phase 2B report's "Exactness" section).  B segments of Lq queries and Lk keys, H heads,
  * D = 128.  sm_scale multiplies q·k (usually 1/sqrt(D)); it must be finite and > 0.
+ *
+ * `workspace` (optional, 16-byte aligned, fwd_workspace_bytes of sattn_quant_query) lets a
+ * problem too small to fill the GPU split the keys of every query tile between two
+ * workgroups: the second starts from the first half's running max (computed from its
+ * scores), so every E4M3 probability equals the sequential recurrence's, and the two
+ * partial results are merged as O = O_1 2^(m_1 - m) + O_2 2^(m_2 - m) (d likewise).  The
+ * workspace must hold zeros before its first use and is left zeroed by every call (its
+ * counters); calls sharing one workspace must not overlap.  NULL (or too small) runs
+ * without the split.  The split changes the FP32 summation order of O and d only.
  * The score of query i and key j in 64-blocks (bq, bk) is (bq: the 32-row block of i
  * when qkv->q_scale_rows = 32)
  *   S = fl32(acc * sigma),  sigma = fl32(fl32(q_scale[bq] * c) * k_scale[bk]),
@@ -176,7 +185,7 @@ SATTN_API sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, satt
  * (rows of padding are not written).  A segment with Lq > 0 and Lk = 0 writes zeros.
  */
 SATTN_API sattn_status sattn_fwd(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D, float sm_scale,
-                       sattn_bf16_out o, void* stream);
+                       sattn_bf16_out o, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * sattn_fwd_varlen — block-diagonal (per-segment) version of sattn_fwd for packed

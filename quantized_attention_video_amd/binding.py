@@ -70,7 +70,8 @@ def lib():
         L.sattn_quant_query.argtypes = [i32, i64, i64, i32, i32, ctypes.POINTER(Sizes)]
         L.sattn_quantize_qkv.argtypes = [BF16In, BF16In, BF16In, i32, i32, i32, i64, i64, vp, vp,
                                          ctypes.POINTER(QKVQuant), vp, ctypes.c_size_t, vp]
-        L.sattn_fwd.argtypes = [ctypes.POINTER(QKVQuant), i32, i32, i32, i32, i32, f32, BF16Out, vp]
+        L.sattn_fwd.argtypes = [ctypes.POINTER(QKVQuant), i32, i32, i32, i32, i32, f32, BF16Out, vp, ctypes.c_size_t,
+                                vp]
         L.sattn_fwd_varlen.argtypes = [ctypes.POINTER(QKVQuant), vp, vp, i32, i64, i64, i32, i32, f32, BF16Out, vp,
                                        ctypes.c_size_t, vp]
         L.sattn_debug_scores.argtypes = [ctypes.POINTER(QKVQuant), vp, vp, i32, i64, i64, i32, i32, f32, i32, i32, i64,
@@ -225,15 +226,24 @@ def sattn_noalloc_scratch_bytes():
     return int(lib().sattn_noalloc_scratch_bytes())
 
 
-def sattn_fwd(quant, B, H, Lq, Lk, sm_scale, out=None, stream=None):
-    """Dense forward; returns (or fills) a BF16 [B, Lq, H, D] tensor (any strided view works)."""
+def sattn_fwd(quant, B, H, Lq, Lk, sm_scale, out=None, stream=None, workspace=None):
+    """Dense forward; returns (or fills) a BF16 [B, Lq, H, D] tensor (any strided view works).
+    workspace: a zero-filled uint8 device tensor of fwd_workspace_bytes (split_workspace())
+    lets problems too small to fill the GPU split their keys between two workgroups."""
     if out is None:
         with _on(stream):
             out = torch.empty((B, Lq, H, D), dtype=torch.bfloat16, device=quant.q.device)
     st = quant.struct()
-    _check(lib().sattn_fwd(ctypes.byref(st), B, H, Lq, Lk, D, float(sm_scale), _view(out, BF16Out),
+    ws, wsb = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (None, 0)
+    _check(lib().sattn_fwd(ctypes.byref(st), B, H, Lq, Lk, D, float(sm_scale), _view(out, BF16Out), ws, wsb,
                            _stream(stream)), "sattn_fwd")
     return out
+
+
+def split_workspace(B, H, Lq, Lk, device="cuda"):
+    """Zero-filled forward workspace for sattn_fwd's key split (kept zeroed by every call)."""
+    s = sattn_quant_query(B, B * Lq, B * Lk, H)
+    return torch.zeros(max(s.fwd_workspace_bytes, 16), dtype=torch.uint8, device=device)
 
 
 def sattn_quantize_kv(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, stream=None, q_scale_rows=64):

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "launch.h"
@@ -41,6 +42,16 @@ QuantWs quant_ws(int nseg, int H) {
 
 size_t fwd_ws(int nseg) { return align_up((size_t)nseg * 4) + align_up(((size_t)nseg + 1) * 4); }
 
+// Key split of the dense forward: used when the split grid still gives every workgroup a CU of
+// its own (2 * grid <= compute units; 128 query tiles at most on 256 CUs) and the segment has
+// at least kSplitMinEpochs key epochs.  One workgroup alone on a CU already keeps its SIMDs
+// most of the way busy, so a split that puts two on a CU gains less than the second half's
+// running-max pass costs.  The first half takes kSplitE1Num / kSplitE1Den of the epochs: the
+// second half's pass over the first half's keys costs about 0.4 of a full epoch each.
+constexpr int64_t kSplitMaxTiles = 128;
+constexpr int kSplitMinEpochs = 16;
+constexpr int kSplitE1Num = 5, kSplitE1Den = 8;
+
 // need_q: the Q buffers take part (false for the fused-Q forward and K/V-only quantization).
 bool quant_bufs_ok(const sattn_qkv_quant* b, bool need_q = true) {
   if (b == nullptr) return false;
@@ -69,6 +80,23 @@ __device__ __align__(256) unsigned char scratch[kScratchBytes];
 constexpr int kMaxDevices = 64;
 std::mutex scratch_mu;
 void* scratch_ptr[kMaxDevices] = {};
+
+int cu_cache[kMaxDevices] = {};
+
+// Compute units of the current device (asked once per device).
+sattn_status cu_count(int* out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SATTN_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return SATTN_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (cu_cache[dev] == 0 &&
+      hipDeviceGetAttribute(&cu_cache[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    cu_cache[dev] = 0;
+    return SATTN_EHIP;
+  }
+  *out = cu_cache[dev];
+  return SATTN_OK;
+}
 
 sattn_status scratch_for_current_device(void** out) {
   int dev = -1;
@@ -113,7 +141,13 @@ sattn_status sattn_quant_query(int nseg, int64_t total_q, int64_t total_k, int H
   out->v_bytes = out->k_bytes;
   out->v_scale_bytes = out->k_mean_bytes;
   out->quant_workspace_bytes = quant_ws(nseg, H).total;
-  out->fwd_workspace_bytes = fwd_ws(nseg);
+  // the key split needs room for its partials only when the grid could be small enough: a
+  // dense problem has between H * total_q / 128 and H * (total_q / 128 + nseg) query tiles
+  const int64_t qpw = attn_queries_per_wg();
+  const int64_t tiles_lo = (int64_t)H * ((total_q + qpw - 1) / qpw);
+  const int64_t tiles_hi = (int64_t)H * (total_q / qpw + nseg);
+  const size_t split = tiles_lo <= kSplitMaxTiles ? split_ws_bytes(std::min(tiles_hi, kSplitMaxTiles)) : 0;
+  out->fwd_workspace_bytes = fwd_ws(nseg) > split ? fwd_ws(nseg) : split;
   return SATTN_OK;
 }
 
@@ -203,7 +237,7 @@ static sattn_status fwd_common(const sattn_qkv_quant* qkv, int H, int D, float s
 static float log2e_scale(float sm_scale) { return (float)((double)sm_scale * 1.4426950408889634); }
 
 static sattn_status fwd_dense(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D, float sm_scale,
-                              sattn_bf16_out o, void* stream) {
+                              sattn_bf16_out o, void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 1 || Lq < 0 || Lk < 0) return SATTN_EINVAL;
   sattn_status st = fwd_common(qkv, H, D, sm_scale, o, true);
   if (st != SATTN_OK) return st;
@@ -224,14 +258,30 @@ static sattn_status fwd_dense(const sattn_qkv_quant* qkv, int B, int H, int Lq, 
   p.max_kblocks = ceil64(Lk);
   const int qpw = attn_queries_per_wg();
   const int64_t ntile = ceil64(Lq) * 64 / qpw + (ceil64(Lq) * 64 % qpw != 0);
-  const int64_t grid = 8 * (int64_t)((H + 7) / 8) * B * ntile;
+  int64_t grid = 8 * (int64_t)((H + 7) / 8) * B * ntile;
   if (grid > kMaxGroups256) return SATTN_EUNSUPPORTED;
+  p.split = 1;
+  const int64_t tiles = (int64_t)B * H * ntile;
+  if (workspace != nullptr && tiles <= kSplitMaxTiles && ceil64(Lk) >= kSplitMinEpochs &&
+      workspace_bytes >= split_ws_bytes(tiles)) {
+    int cus = 0;
+    if (cu_count(&cus) != SATTN_OK) return SATTN_EHIP;
+    if (2 * grid <= cus) {
+      p.split = 2;
+      p.split_e1 = (int)(ceil64(Lk) * kSplitE1Num / kSplitE1Den);
+      p.cnt = static_cast<int32_t*>(workspace);
+      p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + (split_ws_bytes(tiles) -
+                                                                         (size_t)tiles * 2 * kSplitHalfBytes));
+      grid *= 2;
+    }
+  }
   return launch_attention(p, grid, false, static_cast<hipStream_t>(stream)) == hipSuccess ? SATTN_OK : SATTN_EHIP;
 }
 
 sattn_status sattn_fwd(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D, float sm_scale,
-                       sattn_bf16_out o, void* stream) {
-  return fwd_dense(qkv, B, H, Lq, Lk, D, sm_scale, o, stream);
+                       sattn_bf16_out o, void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace != nullptr && !aligned16(workspace)) return SATTN_EINVAL;
+  return fwd_dense(qkv, B, H, Lq, Lk, D, sm_scale, o, workspace, workspace_bytes, stream);
 }
 
 sattn_status sattn_debug_scores(const sattn_qkv_quant* qkv, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,

@@ -116,6 +116,7 @@ __shared__ __attribute__((aligned(16))) uint8_t g_v2[kTileBytes];
 constexpr int kKsLds = 2048;
 __shared__ float g_ks[kKsLds];
 __shared__ float g_qamax[kWaves];  // fused Q preparation: each wave's 32-row amax
+__shared__ int g_split_order;      // key split: how many halves of the tile had finished before this one
 constexpr int kChunksPerTile = kTileBytes / 16 / (kLoaderWaves * 64);  // per loader lane
 static_assert(kChunksPerTile * kLoaderWaves * 64 * 16 == kTileBytes, "tile split");
 
@@ -222,6 +223,51 @@ __device__ __forceinline__ void qk_tile(v16i& acc_t, const uint8_t* Kl, const v4
   for (int i = 0; i < 16; ++i) acc_t[i] = kAccBias;
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc_t = __builtin_amdgcn_mfma_i32_32x32x32_i8(load_k(Kl, lane, t, u), qop[u], acc_t, 0, 0, 0);
+}
+
+// Device-coherent 16-byte store and load through a buffer resource (cache policy SC1: device
+// scope, past the caches that are not coherent across the XCDs).
+constexpr int kBufWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kCoherentAgent = 16;     // the SC1 bit of the instruction's cache policy
+__device__ __forceinline__ void st_coherent16(__amdgpu_buffer_rsrc_t r, int off, float a, float b, float c,
+                                              float d) {
+  const v4f x = {a, b, c, d};
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, x), r, off, 0, kCoherentAgent);
+}
+__device__ __forceinline__ v4f ld_coherent16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherentAgent));
+}
+
+// Key split, second half: the running max over the first np epochs of the segment (the
+// keys of the other half), exactly as the sequential recurrence has it when it reaches the
+// second half: m = max(m, fl32(max_j acc_j * sigma_e)) per epoch.  QK MFMAs and the row max
+// only; the K tiles pass through a three-slot ring with two epochs of prefetch.
+__device__ __forceinline__ float prefix_max(const Pipe& c, const uint8_t* kg0, const_f32* ksc0, int np) {
+  float m = -INFINITY;
+  if (np <= 0) return m;
+  issue_tile(c, kg0, 0, kslot<0>());
+  if (np > 1) issue_tile(c, kg0, 1, kslot<1>());
+  for (int e = 0; e < np; ++e) {
+    if (e + 1 < np) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kChunksPerTile) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    barrier();  // K(e) visible; every wave is done with the slot K(e+2) goes to
+    const int sl = e % kRing;
+    if (e + 2 < np) {
+      const int sn = (e + 2) % kRing;
+      issue_tile(c, kg0, e + 2, sn == 0 ? kslot<0>() : sn == 1 ? kslot<1>() : kslot<2>());
+    }
+    const uint8_t* Kl = sl == 0 ? kslot<0>() : sl == 1 ? kslot<1>() : kslot<2>();
+    v16i a0, a1;
+    qk_tile(a0, Kl, c.qop, c.lane, 0);
+    qk_tile(a1, Kl, c.qop, c.lane, 1);
+    int mx = INT_MIN;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = max(max(mx, a0[r]), a1[r]);
+    mx = xhalf_max(mx);
+    m = fmaxf(m, (float)(mx - kAccBias) * (c.sig_q * ksc0[e]));
+  }
+  barrier();  // every wave is done with the ring before the epoch pipeline reuses it
+  return m;
 }
 
 // Online softmax of epoch e for this lane's query (32 of the 64 keys; the other 32 are in
@@ -456,7 +502,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level addressing in SGPRs
 
   // ---------------------------------------------------------------- work item
-  int s, h;
+  int s, h, half = 0;
   int64_t qt;
   if constexpr (DUMP) {  // the query tiles of one (segment, head) that hold sampled rows
     s = p.dump.seg;
@@ -464,7 +510,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     qt = p.dump.tile0 + blockIdx.x;
   } else {
   const int xcd = blockIdx.x & 7;
-  const int64_t kk = blockIdx.x >> 3;
+  int64_t kk = blockIdx.x >> 3;
+  if (p.split == 2) {  // the two halves of a tile: neighbours on one XCD
+    half = (int)(kk & 1);
+    kk >>= 1;
+  }
   const int nh = xcd < p.H ? (p.H - xcd + 7) / 8 : 0;
   if (nh == 0) return;
   int64_t hl;
@@ -493,8 +543,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   }
   const SegInfo qi = seg_info(p.gq, s, p.o_st);
   const SegInfo ki = seg_info(p.gk, s, 0);
-  const int nkb = (int)ceil_blocks(ki.len);
-  const int last_valid = (int)(ki.len - (int64_t)(nkb - 1) * kBlk);  // keys in the last epoch
+  const int nkb_seg = (int)ceil_blocks(ki.len);
+  // key split: half 0 takes epochs [0, e1), half 1 [e1, nkb_seg) (the partial last one too)
+  const int e1 = p.split == 2 ? min(p.split_e1, nkb_seg - 1) : nkb_seg;
+  const int e0 = half ? e1 : 0;
+  const int nkb = half ? nkb_seg - e1 : e1;
+  const int last_valid = (p.split == 2 && half == 0) ? kBlk : (int)(ki.len - (int64_t)(nkb_seg - 1) * kBlk);
   const int64_t qb = qt * kQBlocksPerWG + (wave >> 1);  // this wave's 64-query block
   const int hq = wave & 1;                              // and which 32 of its queries
   if constexpr (DUMP) {  // no sampled row in this tile (uniform over the workgroup): done
@@ -568,9 +622,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     c.sig_q = p.q_scale[qsi] * p.c32;
   }
   const int64_t ktile0 = (int64_t)h * p.kblk_cap + ki.blk0;
-  c.kg = reinterpret_cast<const uint8_t*>(p.k8) + ktile0 * kTileBytes;
-  c.vg = p.v8 + ktile0 * kTileBytes;
-  c.ksc = (const_f32*)(p.k_scale + ktile0);
+  if (half) c.m = prefix_max(c, reinterpret_cast<const uint8_t*>(p.k8) + ktile0 * kTileBytes,
+                             (const_f32*)(p.k_scale + ktile0), e1);
+  c.kg = reinterpret_cast<const uint8_t*>(p.k8) + (ktile0 + e0) * kTileBytes;
+  c.vg = p.v8 + (ktile0 + e0) * kTileBytes;
+  c.ksc = (const_f32*)(p.k_scale + ktile0 + e0);
   if constexpr (KSL) {  // landed by the barrier before the first step
     for (int i = tid; i < nkb; i += kWaves * 64) g_ks[i] = c.ksc[i];
   } else {
@@ -638,8 +694,60 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   if (nkb > 0) step_last<DUMP, KSL>(c, nfull, last_valid, dump, acc, std::make_integer_sequence<int, kUnroll>{});
 
   // ---------------------------------------------------------------- epilogue
+  float dtot = xhalf_sum(c.dpart);  // = 448 * d
+  if (p.split == 2) {
+    // Both halves store m, d and O of their rows; the half that finishes second merges:
+    // m = max(m_0, m_1), O = O_0 2^(m_0 - m) + O_1 2^(m_1 - m), d likewise, in that order
+    // whichever half merges.  The partials move through device-coherent 16-byte stores and
+    // loads, lane-major so that each instruction covers 1 KiB (they bypass the caches that
+    // are not coherent across the XCDs, so the halves may sit on different XCDs); the stores
+    // are complete before this workgroup's arrival is counted, and the merging half reads
+    // only after it saw the other's count.  Agent-scope fences would write back and
+    // invalidate the whole L2 of the XCD at every tile's end instead.
+    const int64_t ntile = (ceil_blocks(p.gq.L) + kQBlocksPerWG - 1) / kQBlocksPerWG;
+    const int64_t tile = ((int64_t)s * p.H + h) * ntile + qt;
+    const __amdgpu_buffer_rsrc_t pair = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<char*>(p.part) + tile * 2 * kSplitHalfBytes, 0, 2 * kSplitHalfBytes, kBufWord3);
+    const int mine = (half * 4 + wave) * (kSplitHalfBytes / 4) + lane * 16;
+    const int other = ((1 - half) * 4 + wave) * (kSplitHalfBytes / 4) + lane * 16;
+    if (c.active) {  // uniform over the wave
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          st_coherent16(pair, mine + (4 * w + q4) * 1024, c.oacc[w][4 * q4], c.oacc[w][4 * q4 + 1],
+                        c.oacc[w][4 * q4 + 2], c.oacc[w][4 * q4 + 3]);
+      st_coherent16(pair, mine + 16 * 1024, c.m, dtot, 0.f, 0.f);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partials are stored
+    __syncthreads();
+    if (tid == 0) g_split_order = __hip_atomic_fetch_add(p.cnt + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (g_split_order == 0) return;  // the other half merges
+    if (tid == 0) __hip_atomic_store(p.cnt + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // zero for the next call
+    if (!c.active) return;
+    v4f po[17];
+#pragma unroll
+    for (int j = 0; j < 17; ++j) po[j] = ld_coherent16(pair, other + j * 1024);
+    const float m0 = half ? po[16][0] : c.m, m1 = half ? c.m : po[16][0];
+    const float m = fmaxf(m0, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m0 - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+    {
+      const float d0 = half ? po[16][1] : dtot, d1 = half ? dtot : po[16][1];
+      dtot = __builtin_fmaf(d1, a1, d0 * a0);
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+        for (int r3 = 0; r3 < 4; ++r3) {
+          const float x = c.oacc[w][4 * q4 + r3], y = po[4 * w + q4][r3];
+          const float x0 = half ? y : x, x1 = half ? x : y;
+          c.oacc[w][4 * q4 + r3] = __builtin_fmaf(x1, a1, x0 * a0);
+        }
+  }
   if (!c.active) return;
-  const float dtot = xhalf_sum(c.dpart);  // = 448 * d
   const float inv = dtot > 0.f ? 1.0f / dtot : 0.f;
   const int64_t row = qb * kBlk + hq * 32 + (lane & 31);
   if (row >= qi.len) return;

@@ -64,7 +64,21 @@ struct AttnParams {
   int q_scale_shift;    // Q scales per 64-token block: 1 << q_scale_shift (1 or 2)
   const uint16_t* qbf;  // BF16 Q view quantized in the kernel (sattn_fwd_fused), else nullptr
   int64_t qb_sb, qb_st, qb_sh;  // its batch, token and head element strides
+  // Key split (dense problems whose grid leaves CUs idle): 2 = each query tile's epochs are
+  // shared by two workgroups, which merge their partial results; 1 = no split.
+  int split;
+  float* part;   // [tile][half][wave][17][lane] float4: partial O (16) and (m, d) of each half
+  int32_t* cnt;  // [tile]: finished halves; zero between calls
+  int split_e1;  // epochs of the first half: [0, split_e1) and [split_e1, end)
 };
+
+// One half of a split tile: per wave and lane, 16 float4 of O accumulators and one (m, d).
+constexpr int kSplitHalfBytes = 4 * 17 * 64 * 16;
+// Bytes of the key-split workspace for `tiles` query tiles (counters, then partials).
+inline size_t split_ws_bytes(int64_t tiles) {
+  const size_t cnt = ((size_t)tiles * 4 + 255) / 256 * 256;
+  return cnt + (size_t)tiles * 2 * kSplitHalfBytes;
+}
 
 int stats_chunks(int nseg, int H);
 hipError_t launch_quantize(const QuantLaunch& a, hipStream_t stream);

@@ -141,7 +141,7 @@ int run(const char* in_path, const char* out_path) {
                                      stream),
                     "sattn_fwd_varlen");
   else if (good)
-    good = sattn_ok(sattn_fwd(&quant, nseg, H, (int)Lq, (int)Lk, kD, sm_scale, o, stream), "sattn_fwd");
+    good = sattn_ok(sattn_fwd(&quant, nseg, H, (int)Lq, (int)Lk, kD, sm_scale, o, nullptr, 0, stream), "sattn_fwd");
   good = hip_ok(hipStreamSynchronize(stream), "hipStreamSynchronize") && good;
   (void)hipStreamDestroy(stream);
   if (!good) return 1;

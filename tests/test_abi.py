@@ -110,18 +110,19 @@ def test_fwd_validation():
     L = B.lib()
     q = _quant_struct()
     f = L.sattn_fwd
-    assert f(ctypes.byref(q), 1, 1, 64, 64, 64, 0.1, _out(), None) == B.SATTN_EUNSUPPORTED
-    assert f(ctypes.byref(q), 0, 1, 64, 64, 128, 0.1, _out(), None) == B.SATTN_EINVAL
-    assert f(ctypes.byref(q), 1, 1, 64, 64, 128, 0.0, _out(), None) == B.SATTN_EINVAL
-    assert f(ctypes.byref(q), 1, 1, 64, 64, 128, float("nan"), _out(), None) == B.SATTN_EINVAL
-    assert f(ctypes.byref(q), 1, 1, 64, 64, 128, 0.1, _out(ptr=MISALIGNED), None) == B.SATTN_EINVAL
-    assert f(ctypes.byref(q), 1, 1, 64, 64, 128, 0.1, _out(st=4), None) == B.SATTN_EINVAL
-    assert f(ctypes.byref(_quant_struct(cap=0)), 2, 1, 64, 64, 128, 0.1, _out(), None) == B.SATTN_ENOSPACE
-    assert f(None, 1, 1, 64, 64, 128, 0.1, _out(), None) == B.SATTN_EINVAL
-    assert f(ctypes.byref(_quant_struct(rows=16)), 1, 1, 64, 64, 128, 0.1, _out(), None) == B.SATTN_EINVAL
+    assert f(ctypes.byref(q), 1, 1, 64, 64, 64, 0.1, _out(), None, 0, None) == B.SATTN_EUNSUPPORTED
+    assert f(ctypes.byref(q), 0, 1, 64, 64, 128, 0.1, _out(), None, 0, None) == B.SATTN_EINVAL
+    assert f(ctypes.byref(q), 1, 1, 64, 64, 128, 0.0, _out(), None, 0, None) == B.SATTN_EINVAL
+    assert f(ctypes.byref(q), 1, 1, 64, 64, 128, float("nan"), _out(), None, 0, None) == B.SATTN_EINVAL
+    assert f(ctypes.byref(q), 1, 1, 64, 64, 128, 0.1, _out(ptr=MISALIGNED), None, 0, None) == B.SATTN_EINVAL
+    assert f(ctypes.byref(q), 1, 1, 64, 64, 128, 0.1, _out(st=4), None, 0, None) == B.SATTN_EINVAL
+    assert f(ctypes.byref(_quant_struct(cap=0)), 2, 1, 64, 64, 128, 0.1, _out(), None, 0, None) == B.SATTN_ENOSPACE
+    assert f(None, 1, 1, 64, 64, 128, 0.1, _out(), None, 0, None) == B.SATTN_EINVAL
+    assert f(ctypes.byref(_quant_struct(rows=16)), 1, 1, 64, 64, 128, 0.1, _out(), None, 0, None) == B.SATTN_EINVAL
     # 2^31 - 1 queries of 8 heads: 1.3e8 workgroups, beyond one dispatch's 32-bit work-item count
-    assert f(ctypes.byref(_quant_struct(cap=1 << 40)), 1, 8, (1 << 31) - 1, 64, 128, 0.1, _out(), None) \
+    assert f(ctypes.byref(_quant_struct(cap=1 << 40)), 1, 8, (1 << 31) - 1, 64, 128, 0.1, _out(), None, 0, None) \
         == B.SATTN_EUNSUPPORTED
+    assert f(ctypes.byref(q), 1, 1, 64, 64, 128, 0.1, _out(), MISALIGNED, 1 << 20, None) == B.SATTN_EINVAL
     v = L.sattn_fwd_varlen
     assert v(ctypes.byref(q), FAKE, FAKE, 2, 100, 100, 1, 128, 0.1, _out(), FAKE, 4, None) == B.SATTN_ENOSPACE
     assert v(ctypes.byref(q), None, FAKE, 2, 100, 100, 1, 128, 0.1, _out(), FAKE, 1024, None) == B.SATTN_EINVAL

@@ -801,3 +801,157 @@ def test_epoch_checkpoints_against_the_oracle(name, seg, head, q0, step):
     _say(f"[checkpoints] {name} seg {seg} head {head}: {len(rows)} rows x {nep} epochs, {flips} E4M3 bytes at "
          f"rounding midpoints")
     assert flips <= max(2, 1e-4 * len(rows) * Lk), "too many probability bytes differ"
+
+
+# ---------------------------------------------------------------- key split of small grids
+def _ntile(Lq):
+    return -(-(-(-Lq // 64) * 64) // 128)
+
+
+def _splits(Bn, H, Lq, Lk):
+    """The library's rule: both halves of every tile get a CU of their own (2 * grid <= CUs,
+    128 tiles at most) and the keys span at least 16 epochs."""
+    grid = 8 * -(-H // 8) * Bn * _ntile(Lq)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return 2 * grid <= cus and Bn * H * _ntile(Lq) <= 128 and -(-Lk // 64) >= 16
+
+
+def _counter_bytes(tiles):
+    """The split workspace starts with one 32-bit counter per tile, padded to 256 bytes."""
+    return -(-tiles * 4 // 256) * 256
+
+
+def _close_bf16(a, b):
+    """Within one BF16 rounding of each other, plus 2^-10 of the row's largest magnitude.  The
+    split changes only the order in which O and d accumulate; a matrix instruction's
+    accumulation error is relative to the magnitudes it sums, not to the result, so an output
+    element that cancels to near zero (1e-7 against a row maximum of 0.07) can move by more
+    than its own BF16 step while staying 1e-8 of the row's scale."""
+    a, b = a.float(), b.float()
+    row = torch.maximum(a.abs(), b.abs()).amax(dim=-1, keepdim=True)
+    return bool(torch.all((a - b).abs() <= 2.0 ** -7 * torch.maximum(a.abs(), b.abs()) + 2.0 ** -10 * row + 1e-30))
+
+
+def _split_inputs(Bn, H, Lq, Lk, seed, loud_rows=0.0):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((Bn, Lq, H, 128), generator=g)
+    if loud_rows:  # a share of the query rows scaled by 8: large, late running maxima
+        q[torch.rand((Bn, Lq), generator=g) < loud_rows] *= 8.0
+    k = torch.randn((Bn, Lk, H, 128), generator=g)
+    v = torch.randn((Bn, Lk, H, 128), generator=g)
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+def _split_oracle_check(out, q, k, v, sm_scale, label, rows=None):
+    Bn, Lq, H = q.shape[:3]
+    Lk = k.shape[1]
+    cu_q, cu_k = [Lq * i for i in range(Bn + 1)], [Lk * i for i in range(Bn + 1)]
+    oq = O.quantize(W.packed_float64(q), W.packed_float64(k), W.packed_float64(v), cu_q, cu_k)
+    sel = {s: (np.arange(Lq) if rows is None else rows) for s in range(Bn)}
+    ref = O.attention(oq, sm_scale, rows=sel)
+    got = out.float().cpu().numpy().astype(np.float64)
+    for s in range(Bn):
+        _check_output(got[s][sel[s]], ref[s], f"{label} seg {s}")
+
+
+@pytest.mark.parametrize("Bn,H,Lq,Lk", [(1, 1, 128, 4096), (1, 2, 1000, 2049), (1, 8, 2048, 1024), (2, 1, 200, 37810)])
+def test_key_split_long_keys(Bn, H, Lq, Lk):
+    """sattn_fwd with its forward workspace on a grid small enough that both halves of every
+    query tile get a CU of their own: the tile's keys are split between two workgroups (the
+    second first takes the running max over the first half's keys, so every E4M3 probability
+    is the sequential recurrence's) and the halves merge.  20 calls in a row give identical
+    bits and leave the counters at zero; the result differs from the unsplit forward only by
+    the order of the O and d sums, and meets the oracle's tolerance (5% of the query rows
+    scaled by 8)."""
+    _need_gpu()
+    assert _splits(Bn, H, Lq, Lk)
+    q, k, v = _split_inputs(Bn, H, Lq, Lk, seed=Bn * 1000 + H * 100 + Lk, loud_rows=0.05)
+    quant = B.sattn_quantize_qkv(q.cuda(), k.cuda(), v.cuda())
+    plain = B.sattn_fwd(quant, Bn, H, Lq, Lk, 0.09)
+    ws = B.split_workspace(Bn, H, Lq, Lk)
+    outs = [B.sattn_fwd(quant, Bn, H, Lq, Lk, 0.09, workspace=ws) for _ in range(20)]
+    torch.cuda.synchronize()
+    ncnt = _counter_bytes(Bn * H * _ntile(Lq))
+    assert not ws[:ncnt].any(), "the split counters must be left at zero"
+    assert ws[ncnt:].any(), "the split did not run (no partials in the workspace)"
+    out = outs[0]
+    assert all(torch.equal(o, out) for o in outs[1:])
+    assert _close_bf16(out, plain)
+    rows = None if Lq * Lk <= 2_100_000 else np.unique(np.r_[0:8, Lq - 8:Lq, np.arange(0, Lq, 37)])
+    _split_oracle_check(out, q, k, v, 0.09, f"split B={Bn} H={H} Lq={Lq} Lk={Lk}", rows)
+
+
+@pytest.mark.parametrize("name", ["dense_h8_l4096", "ragged_b2_h16_l1000"])
+def test_key_split_not_taken_on_full_grids(name):
+    """Grids whose halves would share CUs run unsplit even with a workspace: the same bits as
+    without one."""
+    c = case(name)
+    inp, quant, w = c["inp"], c["quant"], c["w"]
+    Bn, Lq, H = inp["q"].shape[:3]
+    Lk = inp["k"].shape[1]
+    assert not _splits(Bn, H, Lq, Lk)
+    ws = B.split_workspace(Bn, H, Lq, Lk)
+    out = B.sattn_fwd(quant, Bn, H, Lq, Lk, w.sm_scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert not ws.any()
+    assert torch.equal(out, c["out"])
+
+
+@pytest.mark.parametrize("Lq,Lk", [(64, 1025), (129, 1088), (200, 1345), (96, 1280), (257, 1000), (33, 4097)])
+def test_key_split_small_shapes(Lq, Lk):
+    """Split forward on shapes around tile and epoch boundaries (odd epoch counts, a one-key
+    tail, partial query tiles), against the oracle and the unsplit forward."""
+    _need_gpu()
+    g = torch.Generator().manual_seed(Lq * 7 + Lk)
+    H, Bn = 3, 2
+    assert _splits(Bn, H, Lq, Lk)
+    q = torch.randn((Bn, Lq, H, 128), generator=g).to(torch.bfloat16)
+    k = torch.randn((Bn, Lk, H, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((Bn, Lk, H, 128), generator=g).to(torch.bfloat16)
+    quant = B.sattn_quantize_qkv(q.cuda(), k.cuda(), v.cuda())
+    plain = B.sattn_fwd(quant, Bn, H, Lq, Lk, 0.09)
+    ws = B.split_workspace(Bn, H, Lq, Lk)
+    split = B.sattn_fwd(quant, Bn, H, Lq, Lk, 0.09, workspace=ws)
+    torch.cuda.synchronize()
+    ncnt = _counter_bytes(Bn * H * _ntile(Lq))
+    assert not ws[:ncnt].any() and ws[ncnt:].any()
+    assert _close_bf16(split, plain)
+    cu_q, cu_k = [0, Lq, 2 * Lq], [0, Lk, 2 * Lk]
+    oq = O.quantize(W.packed_float64(q), W.packed_float64(k), W.packed_float64(v), cu_q, cu_k)
+    ref = O.attention(oq, 0.09)
+    got = split.float().cpu().reshape(-1, H, 128).numpy().astype(np.float64)
+    for s in range(Bn):
+        _check_output(got[s * Lq:(s + 1) * Lq], ref[s * Lq:(s + 1) * Lq], f"split Lq={Lq} Lk={Lk} seg {s}")
+
+
+def test_key_split_replays_from_a_captured_graph():
+    """The split forward captured in a HIP graph with its workspace: each replay (eager work
+    and synchronisations between them) equals the eager split result, and the counters stay
+    zero."""
+    _need_gpu()
+    g = torch.Generator().manual_seed(43)
+    H, L = 2, 1100
+    assert _splits(1, H, L, L)
+    q, k, v = (torch.randn((1, L, H, 128), generator=g).to(torch.bfloat16).cuda() for _ in range(3))
+    quant = B.sattn_quantize_qkv(q, k, v)
+    ws = B.split_workspace(1, H, L, L)
+    ref = B.sattn_fwd(quant, 1, H, L, L, 0.09, workspace=ws).clone()
+    out = torch.empty_like(ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        B.sattn_fwd(quant, 1, H, L, L, 0.09, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.sattn_fwd(quant, 1, H, L, L, 0.09, out=out, workspace=ws)
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        assert not ws[:_counter_bytes(H * 9)].any()
+        B.sattn_fwd(quant, 1, H, L, L, 0.09, workspace=ws)  # eager work between the replays
+        torch.cuda.synchronize()
