@@ -1,39 +1,40 @@
 """Throughput of the quantized attention hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--fused-q]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--two-pass]
                 [--latency [--samples S]]
 
 --workload takes any workload of quantized_attention_video_amd/workloads.py; a packed one
-(varlen_h24_4seg) runs sattn_quantize_qkv with cu_seqlens and sattn_fwd_varlen.
+(varlen_h24_4seg) passes cu_seqlens.
 
 A step is one pass of the whole path over one batch of synthetic input already resident
-in HBM: sattn_quantize_qkv (K statistics, INT8 Q/K tiles, E4M3 V tiles) followed by
-sattn_fwd (the fused attention kernel).  The default workload is the H3-like video layer:
-B=1, H=32, L=37,810 packed tokens, D=128, Q/K/V projection-strided slices of one fused
-[L, 3, H, D] BF16 tensor.  `value` is 4*Lq*Lk*D*H per step over the measured step time
-(TOPS).  The attention kernel's own launches are timed with HIP events on the stream it
-runs on; its algorithmic operation count over that time, against the 5.0 POP/s dense
-INT8/FP8 MFMA peak, is the roofline entry.  The CPU baseline times the FP64 oracle on a
-bounded sample of the same workload and extrapolates linearly.
+in HBM: sattn_quantize_qkv with the Q buffers absent (K statistics, mean-smoothed INT8 K
+tiles, E4M3 V tiles) followed by sattn_fwd_fused (the attention kernel, which quantizes
+each workgroup's Q rows to INT8 from the BF16 view before its key loop).  The default
+workload is the H3-like video layer: B=1, H=32, L=37,810 packed tokens, D=128, Q/K/V
+projection-strided slices of one fused [L, 3, H, D] BF16 tensor.  `value` is 4*Lq*Lk*D*H
+per step over the measured step time (TOPS).  The attention kernel's own launches are
+timed with HIP events on the stream it runs on; its algorithmic operation count over that
+time, against the 5.0 POP/s dense INT8/FP8 MFMA peak, is the roofline entry.  The CPU
+baseline times the FP64 oracle on a bounded sample of the same workload and extrapolates
+linearly.
 
 --latency (for the small shapes, e.g. --workload fixed_q128_kv192) reports the per-launch
-time of sattn_fwd (given its forward workspace, so that grids too small for the GPU split
-each query tile's keys between two workgroups; --no-split withholds it) the way the pages
-time their fixed-shape kernel: samples of 20
+time of sattn_fwd the way the pages time their fixed-shape kernel: samples of 20
 back-to-back launches, the per-launch time being a sample's event interval over 20; the
 launches are replayed from a captured HIP graph so that host enqueue time (Python and
-ctypes) does not stretch the interval, with the eager figure beside it.  Its CPU baseline
-is the whole oracle on the whole shape, on one host thread and on all of them.
+ctypes) does not stretch the interval, with the eager figure beside it.  sattn_fwd gets
+its forward workspace (--no-split withholds it), with which grids small enough for both
+halves of every query tile to own a CU split each tile's keys between two workgroups.  Its
+CPU baseline is the whole oracle on the whole shape, on one host thread and on all of them.
 
 --summarize-trace CSV (with the --steps/--warmup of the profiled run) reads a rocprofv3
 kernel-trace CSV of a bench.py run and prints per-kernel launch statistics with the warm-up
 launches and the timed ones apart; --summarize-counters CSV [CSV ...] prints the mean of
 every counter of rocprofv3 --pmc runs per kernel over the timed launches.
 
---fused-q times the other form of the same path: sattn_quantize_qkv for K and V only, then
-sattn_fwd_fused, which quantizes Q inside the attention launch from the BF16 view (the
-outputs are bit-identical).  Its roofline entry carries no traffic figure: the committed
-counter summary is for the two-pass launch.
+--two-pass times the other form of the same path: sattn_quantize_qkv (Q as well) followed
+by sattn_fwd (or sattn_fwd_varlen) over the INT8 Q tiles.  The outputs are bit-identical;
+the fused form saves the Q pass (a BF16 read and an INT8 write of Q) and is the default.
 """
 import argparse
 import hashlib
@@ -47,7 +48,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_TOPS = 5000.0  # MI355X dense INT8 (and FP8) MFMA peak, TOP/s
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_h3_l37810_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_fused_h3_l37810_traffic.txt")
 KERNEL_SRC = os.path.join(ROOT, "quantized_attention_video_amd", "csrc", "attn.hip")
 
 
@@ -340,8 +341,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="h3_video_l37810")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--fused-q", action="store_true",
-                    help="step = K/V-only quantization + sattn_fwd_fused (Q prepared in the attention launch)")
+    ap.add_argument("--two-pass", action="store_true",
+                    help="step = Q/K/V quantization + sattn_fwd over INT8 Q tiles (default: K/V quantization + "
+                         "sattn_fwd_fused, which prepares Q inside the attention launch)")
     ap.add_argument("--latency", action="store_true",
                     help="per-launch time of sattn_fwd on a small dense shape (samples of 20 launches)")
     ap.add_argument("--samples", type=int, default=500, help="--latency: samples of 20 launches")
@@ -393,14 +395,14 @@ def main():
         Bn, Lq, Lk = 1, T, T  # for the byte count below: one packed sequence of T tokens
         cq = torch.tensor(inp["cu_q"], dtype=torch.int32, device="cuda")
         ck = torch.tensor(inp["cu_k"], dtype=torch.int32, device="cuda")
-        quant = B.alloc_quantized(nseg, T, T, H, with_q=not args.fused_q)
+        quant = B.alloc_quantized(nseg, T, T, H, with_q=args.two_pass)
         out = torch.empty((T, H, 128), dtype=torch.bfloat16, device="cuda")
         ws = B.fwd_workspace(nseg)
     else:
         Bn, Lq, H = q.shape[:3]
         Lk = k.shape[1]
         cq = ck = None
-        quant = B.alloc_quantized(Bn, Bn * Lq, Bn * Lk, H, with_q=not args.fused_q)
+        quant = B.alloc_quantized(Bn, Bn * Lq, Bn * Lk, H, with_q=args.two_pass)
         out = torch.empty((Bn, Lq, H, 128), dtype=torch.bfloat16, device="cuda")
 
     def step(ev=None):
@@ -409,7 +411,7 @@ def main():
         B.sattn_quantize_qkv(q, k, v, cq, ck, out=quant, stream=stream)
         if ev:
             ev[1].record(stream)
-        if args.fused_q:
+        if not args.two_pass:
             B.sattn_fwd_fused(quant, q, w.sm_scale, cq, ck, Lk=Lk, out=out, workspace=ws if w.varlen else None,
                               stream=stream)
         elif w.varlen:
@@ -437,13 +439,13 @@ def main():
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
     quant_avg = sum(quant_ms) / len(quant_ms)
     achieved = ops / (fwd_avg * 1e-3) / 1e12
-    traffic = None if args.fused_q else measured_traffic(w.name)
+    traffic = None if args.two_pass else measured_traffic(w.name)
     # algorithmic HBM bytes of the quantization pass: Q read once (2D) and written as INT8
     # (D); K and V read twice each (statistics, then quantization: 8D) and written once (2D)
-    quant_bytes = H * Bn * ((0 if args.fused_q else 3 * 128 * Lq) + 10 * 128 * Lk)
+    quant_bytes = H * Bn * ((3 * 128 * Lq if args.two_pass else 0) + 10 * 128 * Lk)
     copy_rate = copy_gbs(torch)  # after the timed steps
-    step_name = ("sattn_quantize_qkv (K, V) + sattn_fwd_fused" if args.fused_q
-                 else "sattn_quantize_qkv + sattn_fwd_varlen" if w.varlen else "sattn_quantize_qkv + sattn_fwd")
+    step_name = ("sattn_quantize_qkv + sattn_fwd_varlen" if args.two_pass and w.varlen else
+                 "sattn_quantize_qkv + sattn_fwd" if args.two_pass else "sattn_quantize_qkv (K, V) + sattn_fwd_fused")
     result = {
         "metric": ("attention TOPS (4*Lq*Lkv*D*H/s) at L=37,810 D=128; % of MFMA peak" if w.name == "h3_video_l37810"
                    else "attention TOPS (4*Lq*Lkv*D*H/s, summed over segments); % of MFMA peak"),

@@ -170,13 +170,15 @@ SATTN_API sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, satt
  * D = 128.  sm_scale multiplies q·k (usually 1/sqrt(D)); it must be finite and > 0.
  *
  * `workspace` (optional, 16-byte aligned, fwd_workspace_bytes of sattn_quant_query) lets a
- * problem too small to fill the GPU split the keys of every query tile between two
- * workgroups: the second starts from the first half's running max (computed from its
- * scores), so every E4M3 probability equals the sequential recurrence's, and the two
- * partial results are merged as O = O_1 2^(m_1 - m) + O_2 2^(m_2 - m) (d likewise).  The
- * workspace must hold zeros before its first use and is left zeroed by every call (its
- * counters); calls sharing one workspace must not overlap.  NULL (or too small) runs
- * without the split.  The split changes the FP32 summation order of O and d only.
+ * problem whose grid leaves most CUs idle split the keys of every 128-query tile between
+ * two workgroups: taken when both halves of every tile get a CU of their own (at most 128
+ * tiles on a 256-CU device) and the keys span at least 16 epochs of 64.  The second half
+ * starts from the running max over the first half's keys (computed from their scores), so
+ * every E4M3 probability equals the sequential recurrence's, and the two partial results
+ * are merged as O = O_1 2^(m_1 - m) + O_2 2^(m_2 - m) (d likewise).  The workspace must
+ * hold zeros before its first use and its counters are left zeroed by every call; calls
+ * sharing one workspace must not overlap.  NULL (or too small) runs without the split.
+ * The split changes the FP32 summation order of O and d only.
  * The score of query i and key j in 64-blocks (bq, bk) is (bq: the 32-row block of i
  * when qkv->q_scale_rows = 32)
  *   S = fl32(acc * sigma),  sigma = fl32(fl32(q_scale[bq] * c) * k_scale[bk]),

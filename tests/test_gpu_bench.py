@@ -42,7 +42,14 @@ def test_throughput_line_dense():
 def test_throughput_line_packed():
     d = _bench("--workload", "varlen_h24_4seg", "--steps", "2", "--warmup", "1", "--no-cpu-baseline")
     assert all(k in d for k in CONTRACT)
-    assert d["config"]["seqlens"] == [37810, 8192, 1536, 100] and "sattn_fwd_varlen" in d["config"]["step"]
+    assert d["config"]["seqlens"] == [37810, 8192, 1536, 100] and "sattn_fwd_fused" in d["config"]["step"]
+    assert 0 < d["roofline"]["frac"] < 1
+
+
+def test_throughput_line_two_pass():
+    d = _bench("--workload", "varlen_h24_4seg", "--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--two-pass")
+    assert all(k in d for k in CONTRACT)
+    assert d["config"]["step"] == "sattn_quantize_qkv + sattn_fwd_varlen" and d["roofline"]["traffic"] is None
     assert 0 < d["roofline"]["frac"] < 1
 
 
