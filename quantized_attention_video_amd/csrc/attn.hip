@@ -116,6 +116,7 @@ __shared__ __attribute__((aligned(16))) uint8_t g_v2[kTileBytes];
 constexpr int kKsLds = 2048;
 __shared__ float g_ks[kKsLds];
 __shared__ float g_qamax[kWaves];  // fused Q preparation: each wave's 32-row amax
+__shared__ __attribute__((aligned(16))) float g_vs[kD];  // this head's V channel scales, for the epilogue
 __shared__ int g_split_order;      // key split: how many halves of the tile had finished before this one
 constexpr int kChunksPerTile = kTileBytes / 16 / (kLoaderWaves * 64);  // per loader lane
 static_assert(kChunksPerTile * kLoaderWaves * 64 * 16 == kTileBytes, "tile split");
@@ -223,6 +224,14 @@ __device__ __forceinline__ void qk_tile(v16i& acc_t, const uint8_t* Kl, const v4
   for (int i = 0; i < 16; ++i) acc_t[i] = kAccBias;
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc_t = __builtin_amdgcn_mfma_i32_32x32x32_i8(load_k(Kl, lane, t, u), qop[u], acc_t, 0, 0, 0);
+}
+
+// The requests before the first step: K of epochs 0-2 and V of epoch 0.
+__device__ __forceinline__ void issue_first_tiles(const Pipe& c, int nkb) {
+  if (nkb > 0) issue_tile(c, c.kg, 0, kslot<0>());
+  if (nkb > 1) issue_tile(c, c.kg, 1, kslot<1>());
+  if (nkb > 2) issue_tile(c, c.kg, 2, kslot<2>());
+  if (nkb > 0) issue_tile(c, c.vg, 0, vslot<0>());
 }
 
 // Device-coherent 16-byte store and load through a buffer resource (cache policy SC1: device
@@ -585,6 +594,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   // Fused Q preparation (sattn_fwd_fused): lane g*32 + i holds token 32*hq + i of the
   // wave's 64-row block, channels 64g .. 64g+63, as BF16; the block amax goes through LDS
   // to the sibling wave (one 64-row scale) unless each wave has its own 32-row scale.
+  // The first K/V tiles are requested before anything else, so that their latency overlaps
+  // the Q and scale loads (the second half of a split tile first runs its running-max pass
+  // through the same ring and requests them after it).
+  const int64_t ktile0 = (int64_t)h * p.kblk_cap + ki.blk0;
+  c.kg = reinterpret_cast<const uint8_t*>(p.k8) + (ktile0 + e0) * kTileBytes;
+  c.vg = p.v8 + (ktile0 + e0) * kTileBytes;
+  c.ksc = (const_f32*)(p.k_scale + ktile0 + e0);
+  const bool dma_first = half == 0;
+  if (dma_first) issue_first_tiles(c, nkb);
   const bool fused_q = p.qbf != nullptr;
   uint4 qraw[8];
   float qamax = 0.f;
@@ -612,26 +630,39 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
       const int8_t* src = qt_ptr + ((hq * 4 + u) * 64 + lane) * 16;
       c.qop[u] = *reinterpret_cast<const v4i*>(src);
     }
-    // Retire the Q loads here, with a wait the compiler sees: otherwise its wait-count
-    // bookkeeping keeps them pending into the epoch loop and waits on vmcnt before the QK
-    // MFMAs there, which would also wait for the tile requests in flight.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     // fl32(q_scale * c) of this wave's 32 rows: the scale of their 64-row block, or of
     // their own half of it with 32-row Q scales
     const int64_t qsi = (((int64_t)h * p.qblk_cap + qi.blk0 + qb) << p.q_scale_shift) + (p.q_scale_shift ? hq : 0);
     c.sig_q = p.q_scale[qsi] * p.c32;
   }
-  const int64_t ktile0 = (int64_t)h * p.kblk_cap + ki.blk0;
-  if (half) c.m = prefix_max(c, reinterpret_cast<const uint8_t*>(p.k8) + ktile0 * kTileBytes,
-                             (const_f32*)(p.k_scale + ktile0), e1);
-  c.kg = reinterpret_cast<const uint8_t*>(p.k8) + (ktile0 + e0) * kTileBytes;
-  c.vg = p.v8 + (ktile0 + e0) * kTileBytes;
-  c.ksc = (const_f32*)(p.k_scale + ktile0 + e0);
-  if constexpr (KSL) {  // landed by the barrier before the first step
-    for (int i = tid; i < nkb; i += kWaves * 64) g_ks[i] = c.ksc[i];
+  constexpr int kKsPerThread = kKsLds / (kWaves * 64);
+  float ksr[kKsPerThread];
+  if constexpr (KSL) {  // this epoch range's K scales, staged through LDS below
+#pragma unroll
+    for (int j = 0; j < kKsPerThread; ++j) {
+      const int i = tid + j * kWaves * 64;
+      ksr[j] = i < nkb ? c.ksc[i] : 0.f;
+    }
   } else {
     c.ks_next = nkb > 0 ? c.ksc[0] : 0.f;
   }
+  float4 vs4 = make_float4(0.f, 0.f, 0.f, 0.f);  // V channel scales, staged in LDS for the epilogue
+  if (tid < kD / 4) vs4 = reinterpret_cast<const float4*>(p.v_scale + ((int64_t)s * p.H + h) * kD)[tid];
+  // Retire the Q and scale loads here (the tile requests ahead of them too), with a wait the
+  // compiler sees: otherwise its wait-count bookkeeping keeps them pending into the epoch
+  // loop and waits on vmcnt before the QK MFMAs there, which would also wait for the tile
+  // requests in flight.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if (half) c.m = prefix_max(c, reinterpret_cast<const uint8_t*>(p.k8) + ktile0 * kTileBytes,
+                             (const_f32*)(p.k_scale + ktile0), e1);
+  if constexpr (KSL) {  // landed by the barrier before the first step
+#pragma unroll
+    for (int j = 0; j < kKsPerThread; ++j) {
+      const int i = tid + j * kWaves * 64;
+      if (i < nkb) g_ks[i] = ksr[j];
+    }
+  }
+  if (tid < kD / 4) reinterpret_cast<float4*>(g_vs)[tid] = vs4;
 
   Dump dump;
   dump.idx = -1;
@@ -647,10 +678,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
 #pragma unroll
   for (int i = tid; i < kTileBytes / 16; i += kWaves * 64) reinterpret_cast<v4i*>(g_v2)[i] = v4i{0, 0, 0, 0};
   v16i acc[2];
-  if (nkb > 0) issue_tile(c, c.kg, 0, kslot<0>());
-  if (nkb > 1) issue_tile(c, c.kg, 1, kslot<1>());
-  if (nkb > 2) issue_tile(c, c.kg, 2, kslot<2>());
-  if (nkb > 0) issue_tile(c, c.vg, 0, vslot<0>());
+  if (!dma_first) issue_first_tiles(c, nkb);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   barrier();  // Q, K(0), the K scales, the Q row maxima and the zeroed V slot visible
   if constexpr (KSL) c.ks_next = nkb > 0 ? g_ks[0] : 0.f;
@@ -753,18 +781,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   if (row >= qi.len) return;
   if (DUMP && dump.idx < 0) return;  // the checkpoint run writes the sampled rows only
   uint16_t* orow = p.o + qi.elem_base + row * p.o_st + (int64_t)h * p.o_sh;
-  const float* vsc = p.v_scale + ((int64_t)s * p.H + h) * kD;
 #pragma unroll
   for (int w = 0; w < 4; ++w)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int c0 = 32 * w + 8 * q4 + 4 * c.g;
-      const float4 vs = *reinterpret_cast<const float4*>(vsc + c0);
+      const float4 vs = *reinterpret_cast<const float4*>(g_vs + c0);
       const float vsa[4] = {vs.x, vs.y, vs.z, vs.w};
-      uint32_t b[4];
+      float y[4];
 #pragma unroll
-      for (int r3 = 0; r3 < 4; ++r3) b[r3] = f32_to_bf16_bits((c.oacc[w][4 * q4 + r3] * inv) * vsa[r3]);
-      *reinterpret_cast<uint2*>(orow + c0) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+      for (int r3 = 0; r3 < 4; ++r3) y[r3] = (c.oacc[w][4 * q4 + r3] * inv) * vsa[r3];
+      *reinterpret_cast<uint2*>(orow + c0) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
     }
 }
 

@@ -91,11 +91,13 @@ __device__ __forceinline__ void unpack8(const uint4& raw, float x[8]) {
   x[6] = bf16_lo(raw.w); x[7] = bf16_hi(raw.w);
 }
 
-// Round-to-nearest-even float → BF16 bits (inputs are finite here).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two FP32 values rounded to BF16 (nearest, ties to even), packed low | high << 16: one
+// v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
