@@ -219,6 +219,8 @@ typedef struct {
   float* ro;      /* [rows][nep][128]: the running output RO = sum_j e4m3(448 P_j) * v8_j
                      (v8_j the E4M3 code values; the FP32 accumulators) after epoch e          */
   int64_t nep;    /* epochs recorded: e < nep (later epochs are not written)                  */
+  float* rcp;     /* [rows]: the epilogue's final reciprocal fl32(1 / (448 d)) of the row's
+                     denominator after its last epoch (0 for a row without keys)              */
 } sattn_checkpoints;
 
 /*

@@ -45,7 +45,7 @@ class QKVQuant(ctypes.Structure):
 class Checkpoints(ctypes.Structure):
     _fields_ = [("acc", ctypes.c_void_p), ("s", ctypes.c_void_p), ("ld", ctypes.c_int64), ("m", ctypes.c_void_p),
                 ("d", ctypes.c_void_p), ("alpha", ctypes.c_void_p), ("p8", ctypes.c_void_p), ("ro", ctypes.c_void_p),
-                ("nep", ctypes.c_int64)]
+                ("nep", ctypes.c_int64), ("rcp", ctypes.c_void_p)]
 
 
 class Sizes(ctypes.Structure):
@@ -320,8 +320,8 @@ def sattn_debug_scores(quant, sm_scale, seg, head, q_begin, q_end, q_step=1, Lq=
     `quant` was sized for).  ld: keys per dumped score row (default Lk); nep: epochs of
     per-epoch checkpoints (0: none).  Returns a dict of device tensors: acc and s
     ([rows, ld], with scores=True), m, d, alpha ([rows, nep]), p8 ([rows, nep, 64]) and ro
-    ([rows, nep, 128]) when nep > 0, and out, the forward output (the sampled rows of
-    `head` only are written)."""
+    ([rows, nep, 128]) when nep > 0, rcp ([rows], the epilogue's 1 / (448 d)), and out, the
+    forward output (the sampled rows of `head` only are written)."""
     dev = quant.k.device
     varlen = cu_seqlens_q is not None
     if varlen:
@@ -339,12 +339,13 @@ def sattn_debug_scores(quant, sm_scale, seg, head, q_begin, q_end, q_step=1, Lq=
                 r[n] = torch.zeros((rows, nep), dtype=torch.float32, device=dev)
             r["p8"] = torch.zeros((rows, nep, 64), dtype=torch.uint8, device=dev)
             r["ro"] = torch.zeros((rows, nep, D), dtype=torch.float32, device=dev)
+        r["rcp"] = torch.zeros((rows,), dtype=torch.float32, device=dev)
         if out is None:
             shape = (Lq, quant.H, D) if varlen else (quant.nseg, Lq, quant.H, D)
             out = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
     r["out"] = out
     ck = Checkpoints(_ptr(r.get("acc")), _ptr(r.get("s")), ld if scores else 0, _ptr(r.get("m")), _ptr(r.get("d")),
-                     _ptr(r.get("alpha")), _ptr(r.get("p8")), _ptr(r.get("ro")), nep)
+                     _ptr(r.get("alpha")), _ptr(r.get("p8")), _ptr(r.get("ro")), nep, _ptr(r.get("rcp")))
     st = quant.struct()
     _check(lib().sattn_debug_scores(ctypes.byref(st), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), quant.nseg, Lq, Lk,
                                     quant.H, D, float(sm_scale), seg, head, q_begin, q_end, q_step, ctypes.byref(ck),

@@ -327,6 +327,7 @@ sattn_status sattn_debug_scores(const sattn_qkv_quant* qkv, const int32_t* cu_se
   DumpParams& d = p.dump;
   d.acc = ck->acc; d.s = ck->s; d.ld = ck->ld;
   d.m = ck->m; d.d = ck->d; d.alpha = ck->alpha; d.p8 = ck->p8; d.ro = ck->ro; d.nep = ck->nep;
+  d.rcp = ck->rcp;
   d.seg = seg; d.head = head;
   d.q0 = q_begin; d.q1 = q_end; d.qstep = q_step;
   const int qpw = attn_queries_per_wg();

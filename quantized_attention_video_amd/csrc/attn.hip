@@ -780,6 +780,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   const int64_t row = qb * kBlk + hq * 32 + (lane & 31);
   if (row >= qi.len) return;
   if (DUMP && dump.idx < 0) return;  // the checkpoint run writes the sampled rows only
+  if (DUMP && p.dump.rcp != nullptr && c.g == 0) p.dump.rcp[dump.idx] = inv;
   uint16_t* orow = p.o + qi.elem_base + row * p.o_st + (int64_t)h * p.o_sh;
 #pragma unroll
   for (int w = 0; w < 4; ++w)

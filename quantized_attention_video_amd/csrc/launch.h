@@ -38,6 +38,7 @@ struct DumpParams {
   uint8_t* p8;           // [rows][nep][64]
   float* ro;             // [rows][nep][128]
   int64_t nep;
+  float* rcp;            // [rows]: the epilogue's 1 / (448 d)
   int seg, head;
   int64_t q0, q1, qstep;
   int64_t tile0;  // first query tile of the launch (workgroup b takes tile tile0 + b)

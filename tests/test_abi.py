@@ -153,7 +153,7 @@ def test_noalloc_validation():
 
 
 def _ck(**kw):
-    c = dict(acc=FAKE, s=FAKE, ld=64, m=None, d=None, alpha=None, p8=None, ro=None, nep=0)
+    c = dict(acc=FAKE, s=FAKE, ld=64, m=None, d=None, alpha=None, p8=None, ro=None, nep=0, rcp=None)
     c.update(kw)
     return B.Checkpoints(*(c[n] for n, _ in B.Checkpoints._fields_))
 

@@ -730,7 +730,9 @@ def test_epoch_checkpoints_against_the_oracle(name, seg, head, q0, step):
         FP8 matrix instruction (E4M3 products are exact, but the instruction adds its 64
         products and the accumulator with less than FP32 precision: about 2^-14 of the sum
         of their magnitudes on gfx950, measured; the bound allows 2^-11), the rescale and
-        the flipped bytes.
+        the flipped bytes;
+      * the epilogue's final reciprocal 1 / (448 d): the correctly rounded binary32
+        reciprocal of the kernel's own d, and within d's bound of the oracle's.
     The hardware exp2 is not correctly rounded, so alpha, d and RO cannot be compared bit
     for bit."""
     c = case(name)
@@ -801,6 +803,13 @@ def test_epoch_checkpoints_against_the_oracle(name, seg, head, q0, step):
     _say(f"[checkpoints] {name} seg {seg} head {head}: {len(rows)} rows x {nep} epochs, {flips} E4M3 bytes at "
          f"rounding midpoints")
     assert flips <= max(2, 1e-4 * len(rows) * Lk), "too many probability bytes differ"
+    # the final reciprocal: the correctly rounded binary32 1/x of the kernel's own final d
+    # (units of 448 P), and within d's bound of the oracle's 1 / (448 d)
+    rcp = r["rcp"][:len(rows)].cpu().numpy()
+    d_last = g["d"][:, nep - 1].astype(np.float32)
+    assert np.array_equal(rcp, np.float32(1.0) / d_last), "rcp is not fl32(1 / d)"
+    ref_rcp = 1.0 / (448.0 * cps[-1]["d"])
+    assert np.all(np.abs(rcp - ref_rcp) <= ref_rcp * (tol_d / dref + 2.0 ** -24)), "rcp against the oracle"
 
 
 # ---------------------------------------------------------------- key split of small grids
