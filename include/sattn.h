@@ -259,7 +259,9 @@ SATTN_API sattn_status sattn_debug_scores(const sattn_qkv_quant* qkv, const int3
  * and q_scale are not read and may be NULL).
  *
  *   dense  (cu_seqlens_q == cu_seqlens_k == NULL): nseg segments of Lq queries and Lk
- *          keys; q and o are [nseg, Lq, H, D] views; workspace may be NULL.
+ *          keys; q and o are [nseg, Lq, H, D] views; workspace may be NULL, or (16-byte
+ *          aligned, fwd_workspace_bytes) enables the key split of small grids exactly as
+ *          in sattn_fwd (same rule, same results, same zero-counter contract).
  *   varlen (both non-NULL): the cu_seqlens arrays given to sattn_quantize_qkv; Lq is the
  *          number of packed query tokens the q and o views hold, Lk the packed key
  *          tokens; workspace: fwd_workspace_bytes (16-byte aligned), scratch.

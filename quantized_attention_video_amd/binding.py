@@ -264,8 +264,10 @@ def sattn_quantize_kv(q, k, v, cu_seqlens_q=None, cu_seqlens_k=None, stream=None
 def sattn_fwd_fused(kv, q, sm_scale, cu_seqlens_q=None, cu_seqlens_k=None, Lk=None, out=None, workspace=None,
                     stream=None):
     """Forward with the Q preparation in the attention launch.  Dense: q is a [B, Lq, H, D]
-    view and Lk the keys per segment; varlen: q is packed [T, H, D] and Lk the packed key
-    tokens.  Returns (or fills) the BF16 output shaped like q."""
+    view and Lk the keys per segment (an optional zero-filled `workspace`, see
+    split_workspace, enables the key split of small grids as in sattn_fwd); varlen: q is
+    packed [T, H, D] and Lk the packed key tokens.  Returns (or fills) the BF16 output
+    shaped like q."""
     if Lk is None:
         raise ValueError("Lk (keys per segment, or packed key tokens) is required")
     varlen = cu_seqlens_q is not None
@@ -277,7 +279,7 @@ def sattn_fwd_fused(kv, q, sm_scale, cu_seqlens_q=None, cu_seqlens_k=None, Lk=No
         ws, wsb = workspace.data_ptr(), workspace.numel()
     else:
         nseg, Lq, H = q.shape[0], q.shape[1], q.shape[2]
-        ws, wsb = None, 0
+        ws, wsb = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
     if out is None:
         with _on(stream):
             out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)

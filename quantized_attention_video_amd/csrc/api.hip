@@ -236,6 +236,27 @@ static sattn_status fwd_common(const sattn_qkv_quant* qkv, int H, int D, float s
 
 static float log2e_scale(float sm_scale) { return (float)((double)sm_scale * 1.4426950408889634); }
 
+// The key split of a dense forward (p.split = 2, grid doubled, the workspace's counters and
+// partials wired in) when the workspace is given and large enough, the keys span at least
+// kSplitMinEpochs epochs and both halves of every tile get a CU of their own; else no split.
+static sattn_status plan_split(AttnParams& p, int64_t& grid, int64_t tiles, int64_t Lk, void* workspace,
+                               size_t workspace_bytes) {
+  p.split = 1;
+  if (workspace == nullptr || tiles > kSplitMaxTiles || ceil64(Lk) < kSplitMinEpochs ||
+      workspace_bytes < split_ws_bytes(tiles))
+    return SATTN_OK;
+  int cus = 0;
+  if (cu_count(&cus) != SATTN_OK) return SATTN_EHIP;
+  if (2 * grid > cus) return SATTN_OK;
+  p.split = 2;
+  p.split_e1 = (int)(ceil64(Lk) * kSplitE1Num / kSplitE1Den);
+  p.cnt = static_cast<int32_t*>(workspace);
+  p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    (split_ws_bytes(tiles) - (size_t)tiles * 2 * kSplitHalfBytes));
+  grid *= 2;
+  return SATTN_OK;
+}
+
 static sattn_status fwd_dense(const sattn_qkv_quant* qkv, int B, int H, int Lq, int Lk, int D, float sm_scale,
                               sattn_bf16_out o, void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 1 || Lq < 0 || Lk < 0) return SATTN_EINVAL;
@@ -260,21 +281,8 @@ static sattn_status fwd_dense(const sattn_qkv_quant* qkv, int B, int H, int Lq, 
   const int64_t ntile = ceil64(Lq) * 64 / qpw + (ceil64(Lq) * 64 % qpw != 0);
   int64_t grid = 8 * (int64_t)((H + 7) / 8) * B * ntile;
   if (grid > kMaxGroups256) return SATTN_EUNSUPPORTED;
-  p.split = 1;
-  const int64_t tiles = (int64_t)B * H * ntile;
-  if (workspace != nullptr && tiles <= kSplitMaxTiles && ceil64(Lk) >= kSplitMinEpochs &&
-      workspace_bytes >= split_ws_bytes(tiles)) {
-    int cus = 0;
-    if (cu_count(&cus) != SATTN_OK) return SATTN_EHIP;
-    if (2 * grid <= cus) {
-      p.split = 2;
-      p.split_e1 = (int)(ceil64(Lk) * kSplitE1Num / kSplitE1Den);
-      p.cnt = static_cast<int32_t*>(workspace);
-      p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + (split_ws_bytes(tiles) -
-                                                                         (size_t)tiles * 2 * kSplitHalfBytes));
-      grid *= 2;
-    }
-  }
+  st = plan_split(p, grid, (int64_t)B * H * ntile, Lk, workspace, workspace_bytes);
+  if (st != SATTN_OK) return st;
   return launch_attention(p, grid, false, static_cast<hipStream_t>(stream)) == hipSuccess ? SATTN_OK : SATTN_EHIP;
 }
 
@@ -385,7 +393,8 @@ sattn_status sattn_fwd_fused(const sattn_qkv_quant* kv, sattn_bf16_in q, const i
   sattn_status st = fwd_common(kv, H, D, sm_scale, o, !varlen, false);
   if (st != SATTN_OK) return st;
   if (!view_ok(q.ptr, q.stride_b, q.stride_t, q.stride_h, !varlen)) return SATTN_EINVAL;
-  if (varlen && (workspace == nullptr || !aligned16(workspace))) return SATTN_EINVAL;
+  if (varlen && workspace == nullptr) return SATTN_EINVAL;
+  if (workspace != nullptr && !aligned16(workspace)) return SATTN_EINVAL;
   if (varlen && workspace_bytes < fwd_ws(nseg)) return SATTN_ENOSPACE;
   if (kv->kblk_cap < nseg || (!varlen && kv->kblk_cap < (int64_t)nseg * ceil64(Lk))) return SATTN_ENOSPACE;
   const int64_t k_clip = varlen ? (Lk < clip_for_cap(kv->kblk_cap, nseg) ? Lk : clip_for_cap(kv->kblk_cap, nseg))
@@ -406,9 +415,13 @@ sattn_status sattn_fwd_fused(const sattn_qkv_quant* kv, sattn_bf16_in q, const i
   p.qbf = static_cast<const uint16_t*>(q.ptr);
   p.qb_sb = q.stride_b; p.qb_st = q.stride_t; p.qb_sh = q.stride_h;
   const int qpw = attn_queries_per_wg();
-  const int64_t grid = varlen ? 8 * (int64_t)((H + 7) / 8) * (Lq / qpw + nseg + 1)
-                              : 8 * (int64_t)((H + 7) / 8) * nseg * ((ceil64(Lq) * 64 + qpw - 1) / qpw);
+  const int64_t ntile = (ceil64(Lq) * 64 + qpw - 1) / qpw;
+  int64_t grid = varlen ? 8 * (int64_t)((H + 7) / 8) * (Lq / qpw + nseg + 1) : 8 * (int64_t)((H + 7) / 8) * nseg * ntile;
   if (grid > kMaxGroups256) return SATTN_EUNSUPPORTED;
+  if (!varlen) {  // dense: the key split, as in sattn_fwd
+    st = plan_split(p, grid, (int64_t)nseg * H * ntile, Lk, workspace, workspace_bytes);
+    if (st != SATTN_OK) return st;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (varlen) {
     p.order = static_cast<int32_t*>(workspace);

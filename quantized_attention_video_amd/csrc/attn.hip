@@ -234,6 +234,36 @@ __device__ __forceinline__ void issue_first_tiles(const Pipe& c, int nkb) {
   if (nkb > 0) issue_tile(c, c.vg, 0, vslot<0>());
 }
 
+// Fused Q preparation, second part: the INT8 operands and fl32(q_scale * c) of this wave's
+// 32 rows from their BF16 values, with the quantizer's arithmetic (fl32 scale, RNE codes in
+// [-127, 127], the zero-block rule); the 64-row block amax combines the sibling wave's,
+// which must be visible in LDS.
+__device__ __forceinline__ void fused_q_operands(Pipe& c, const uint4 (&qraw)[8], float qamax, const AttnParams& p,
+                                                 int wave) {
+  const float amax = p.q_scale_shift ? qamax : fmaxf(qamax, g_qamax[wave ^ 1]);
+  const float rcp = 127.0f / amax;
+  const bool zero = !(amax > 0.f) || isinf(rcp);  // the quantizer's zero-block rule
+  const float scale = zero ? 0.f : amax / 127.0f;
+  const float inv = zero ? 0.f : rcp;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {  // word w of operand u: channels 64g + 16u + 4w .. +3
+      float x[8];
+      unpack8(qraw[2 * u + (w >> 1)], x);
+      uint32_t word = 0u;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        float qv = rintf(x[4 * (w & 1) + b] * inv);
+        qv = fminf(fmaxf(qv, -127.f), 127.f);
+        word |= ((uint32_t)((int)qv) & 0xffu) << (8 * b);
+      }
+      c.qop[u][w] = (int)word;
+    }
+  }
+  c.sig_q = scale * p.c32;
+}
+
 // Device-coherent 16-byte store and load through a buffer resource (cache policy SC1: device
 // scope, past the caches that are not coherent across the XCDs).
 constexpr int kBufWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
@@ -653,8 +683,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   // loop and waits on vmcnt before the QK MFMAs there, which would also wait for the tile
   // requests in flight.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  if (half) c.m = prefix_max(c, reinterpret_cast<const uint8_t*>(p.k8) + ktile0 * kTileBytes,
-                             (const_f32*)(p.k_scale + ktile0), e1);
+  if (half) {  // the second half of a split tile: the running max over the first half's keys
+    if (fused_q) {  // which needs this wave's Q operands first
+      barrier();    // the sibling wave's row maximum in LDS
+      if (c.active) fused_q_operands(c, qraw, qamax, p, wave);
+    }
+    c.m = prefix_max(c, reinterpret_cast<const uint8_t*>(p.k8) + ktile0 * kTileBytes,
+                     (const_f32*)(p.k_scale + ktile0), e1);
+  }
   if constexpr (KSL) {  // landed by the barrier before the first step
 #pragma unroll
     for (int j = 0; j < kKsPerThread; ++j) {
@@ -682,30 +718,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   barrier();  // Q, K(0), the K scales, the Q row maxima and the zeroed V slot visible
   if constexpr (KSL) c.ks_next = nkb > 0 ? g_ks[0] : 0.f;
-  if (fused_q && c.active) {  // the quantizer's arithmetic: fl32 scale, RNE codes in [-127, 127]
-    const float amax = p.q_scale_shift ? qamax : fmaxf(qamax, g_qamax[wave ^ 1]);
-    const float rcp = 127.0f / amax;
-    const bool zero = !(amax > 0.f) || isinf(rcp);  // the quantizer's zero-block rule
-    const float scale = zero ? 0.f : amax / 127.0f;
-    const float inv = zero ? 0.f : rcp;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {  // word w of operand u: channels 64g + 16u + 4w .. +3
-        float x[8];
-        unpack8(qraw[2 * u + (w >> 1)], x);
-        uint32_t word = 0u;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          float qv = rintf(x[4 * (w & 1) + b] * inv);
-          qv = fminf(fmaxf(qv, -127.f), 127.f);
-          word |= ((uint32_t)((int)qv) & 0xffu) << (8 * b);
-        }
-        c.qop[u][w] = (int)word;
-      }
-    }
-    c.sig_q = scale * p.c32;
-  }
+  if (fused_q && !half && c.active) fused_q_operands(c, qraw, qamax, p, wave);
   if (nkb > 0) {
     qk_tile(acc[0], kslot<0>(), c.qop, lane, 0);
     qk_tile(acc[1], kslot<0>(), c.qop, lane, 1);

@@ -128,6 +128,15 @@ def test_fwd_validation():
     assert v(ctypes.byref(q), None, FAKE, 2, 100, 100, 1, 128, 0.1, _out(), FAKE, 1024, None) == B.SATTN_EINVAL
     assert v(ctypes.byref(q), FAKE, FAKE, 2, 100, 100, 1, 128, 0.1, _out(), None, 1024, None) == B.SATTN_EINVAL
     assert v(ctypes.byref(q), FAKE, FAKE, 2, 100, -1, 1, 128, 0.1, _out(), FAKE, 1024, None) == B.SATTN_EINVAL
+    g = L.sattn_fwd_fused  # (kv, q, cu_q, cu_k, nseg, H, Lq, Lk, D, sm_scale, o, workspace, bytes, stream)
+    assert g(ctypes.byref(q), _in(), None, None, 1, 1, 64, 64, 64, 0.1, _out(), None, 0, None) == B.SATTN_EUNSUPPORTED
+    assert g(ctypes.byref(q), _in(ptr=MISALIGNED), None, None, 1, 1, 64, 64, 128, 0.1, _out(), None, 0, None) \
+        == B.SATTN_EINVAL
+    # dense: the workspace is optional (the key split) but must be aligned; packed: required
+    assert g(ctypes.byref(q), _in(), None, None, 1, 1, 64, 64, 128, 0.1, _out(), MISALIGNED, 1 << 20, None) \
+        == B.SATTN_EINVAL
+    assert g(ctypes.byref(q), _in(), FAKE, FAKE, 2, 1, 100, 100, 128, 0.1, _out(), None, 1024, None) == B.SATTN_EINVAL
+    assert g(ctypes.byref(q), _in(), FAKE, FAKE, 2, 1, 100, 100, 128, 0.1, _out(), FAKE, 4, None) == B.SATTN_ENOSPACE
 
 
 def test_noalloc_validation():

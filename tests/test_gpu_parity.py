@@ -870,8 +870,8 @@ def test_key_split_long_keys(Bn, H, Lq, Lk):
     second first takes the running max over the first half's keys, so every E4M3 probability
     is the sequential recurrence's) and the halves merge.  20 calls in a row give identical
     bits and leave the counters at zero; the result differs from the unsplit forward only by
-    the order of the O and d sums, and meets the oracle's tolerance (5% of the query rows
-    scaled by 8)."""
+    the order of the O and d sums, equals the fused-Q forward's split bit for bit, and meets
+    the oracle's tolerance (5% of the query rows scaled by 8)."""
     _need_gpu()
     assert _splits(Bn, H, Lq, Lk)
     q, k, v = _split_inputs(Bn, H, Lq, Lk, seed=Bn * 1000 + H * 100 + Lk, loud_rows=0.05)
@@ -886,6 +886,15 @@ def test_key_split_long_keys(Bn, H, Lq, Lk):
     out = outs[0]
     assert all(torch.equal(o, out) for o in outs[1:])
     assert _close_bf16(out, plain)
+    # the fused-Q forward splits by the same rule (its Q operands are ready before the second
+    # half's running-max pass): the same bits
+    qd = q.cuda()
+    kv = B.sattn_quantize_kv(qd, k.cuda(), v.cuda())
+    ws2 = B.split_workspace(Bn, H, Lq, Lk)
+    fused = B.sattn_fwd_fused(kv, qd, 0.09, Lk=Lk, workspace=ws2)
+    torch.cuda.synchronize()
+    assert not ws2[:ncnt].any() and ws2[ncnt:].any()
+    assert torch.equal(fused, out), "fused-Q split differs from the two-pass split"
     rows = None if Lq * Lk <= 2_100_000 else np.unique(np.r_[0:8, Lq - 8:Lq, np.arange(0, Lq, 37)])
     _split_oracle_check(out, q, k, v, 0.09, f"split B={Bn} H={H} Lq={Lq} Lk={Lk}", rows)
 
