@@ -1,11 +1,11 @@
 /*
  * sattn.h — C ABI of the MI355X (gfx950) quantized video-DiT self-attention library.
  *
- * The numerical program follows the pages "h3-blackwell-runtime/PERFORMANCE_ROADMAP.md"
+ * The numerical program follows the pages "H3 Performance Roadmap"
  * (sections "Measured GB10 Baseline" → "SageAttention 2.2.0 internals", the Sage2 phase
  * decomposition paragraph after "The fresh block kernel-time distribution", and "Phase 4:
- * Dense Sage-Compatible Attention") and "research/vortex_exact_attention/
- * PHASE2B_ALIGNED_REPORT.md" (sections "Decision" and "Exactness"):
+ * Dense Sage-Compatible Attention") and "Phase 2B Aligned Numerical Prototype" (sections
+ * "Decision" and "Exactness"):
  *
  *   1. K smoothing: subtract the per-(sequence, head, channel) mean of K.
  *   2. Q and smoothed K → symmetric INT8, one FP32 scale per 64-token block.

@@ -6,9 +6,8 @@ anything from this package.  The HIP library never calls it, and it shares no co
 headers, tables or constants with the HIP path.
 
 The oracle is a plain, slow, FP64 restatement of the numerical program that the pages
-"h3-blackwell-runtime/PERFORMANCE_ROADMAP.md" and
-"research/vortex_exact_attention/PHASE2B_ALIGNED_REPORT.md" describe, with every rounding
-step written out explicitly (``oracle.codecs``).  ``oracle.sattn`` holds the program.
+"H3 Performance Roadmap" and "Phase 2B Aligned Numerical Prototype" describe, with every
+rounding step written out explicitly (``oracle.codecs``).  ``oracle.sattn`` holds the program.
 
 Pins (tests/test_oracle_pins.py, tests/test_codecs.py) tie it to things other than
 itself: the textbook softmax attention it must reduce to when rounding is switched

@@ -1,9 +1,9 @@
 """FP64 oracle of the quantized attention program (test infrastructure only).
 
-Sources (the pages): "h3-blackwell-runtime/PERFORMANCE_ROADMAP.md", the Sage2 phase
+Sources (the pages): "H3 Performance Roadmap", the Sage2 phase
 decomposition (K smoothing, Q/K INT8 quantization, V transpose/FP8 quantization, fused
 mainloop) and "Phase 4: Dense Sage-Compatible Attention" (per-warp INT8 Q/K, FP8 V
-policy, K smoothing); "research/vortex_exact_attention/PHASE2B_ALIGNED_REPORT.md",
+policy, K smoothing); "Phase 2B Aligned Numerical Prototype",
 sections "Decision" (three increasing K64 epochs over KV=192) and "Exactness" (INT32 to
 FP32 QK scores, per-epoch online-softmax m and d, E4M3 probability words, FP32 rescale
 values, PV partials into FP32 RO, final reciprocal, BF16 output).

@@ -1,12 +1,11 @@
 // Fused INT8-QK / FP8-PV attention forward for gfx950.
 //
-// Numerical program: "research/vortex_exact_attention/PHASE2B_ALIGNED_REPORT.md",
-// sections "Decision" and "Exactness" (INT32 scores converted to FP32, online softmax
-// with per-epoch m and d over increasing 64-key epochs, E4M3 probability words, FP32
-// rescale values, P.V accumulated into an FP32 running output, final reciprocal, BF16
-// output), and the fused-mainloop description of "h3-blackwell-runtime/
-// PERFORMANCE_ROADMAP.md" (QK and PV alternate on separate tensor sub-pipelines while the
-// softmax occupies the vector pipes).  The pages' GB10 kernel is warp-specialised with
+// Numerical program: the "Phase 2B Aligned Numerical Prototype" report, sections
+// "Decision" and "Exactness" (INT32 scores converted to FP32, online softmax with
+// per-epoch m and d over increasing 64-key epochs, E4M3 probability words, FP32 rescale
+// values, P.V accumulated into an FP32 running output, final reciprocal, BF16 output), and
+// the fused-mainloop description of the "H3 Performance Roadmap" (QK and PV alternate on
+// separate tensor sub-pipelines while the softmax occupies the vector pipes).  The pages' GB10 kernel is warp-specialised with
 // mbarriers; this one is designed for CDNA4 instead:
 //
 //  * One workgroup = 4 waves = 128 queries of one (segment, head); two workgroups share a
@@ -35,12 +34,17 @@
 //    tile of epoch e is consumed, the QK MFMAs of epoch e+1 into the same registers.  No
 //    MFMA result is waited for inside a step, and matrix cores and vector ALUs work at
 //    the same time.
-//  * The segment's K block scales are copied to LDS once (no scalar load in flight during
-//    a step).  With sattn_fwd_fused the workgroup also quantizes its own queries from the
-//    BF16 view in the prologue, with the quantizer's arithmetic.
+//  * The segment's K block scales and the head's V channel scales are copied to LDS in
+//    the prologue, whose first requests are the K/V tiles (no scalar load in flight
+//    during a step, no global load in the epilogue).  With sattn_fwd_fused the workgroup
+//    also quantizes its own queries from the BF16 view, with the quantizer's arithmetic.
 //  * The O rescale by alpha runs only in the lanes whose row max changed, and not at all
 //    when no row of the wave changed (alpha is then exactly 1, so skipping is
 //    bit-identical).
+//  * Key split (a workspace given, both halves of every tile on a CU of their own): two
+//    workgroups share a tile's keys; the second first takes the running max over the
+//    first half's scores, so every probability word is the sequential recurrence's, and
+//    the one that finishes second merges the other's partial O, m and d.
 //  * Work items (segment, head, 128-query tile) are ordered so that consecutive
 //    workgroups dispatched to one XCD (workgroup b runs on XCD b mod 8) take the same
 //    head and neighbouring query tiles, so the CUs of an XCD stream the same K/V tiles

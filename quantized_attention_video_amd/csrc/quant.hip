@@ -1,9 +1,9 @@
 // Quantization of Q, K, V for the INT8-QK / FP8-PV attention forward (gfx950).
 //
-// Follows the preparation phases that the pages "h3-blackwell-runtime/
-// PERFORMANCE_ROADMAP.md" separate out for SageAttention 2.2.0 (K smoothing, Q/K INT8
-// quantization, V transpose + FP8 quantization; the Sage2 decomposition paragraph and
-// "Phase 4: Dense Sage-Compatible Attention").  All three passes are HBM-bound streams:
+// Follows the preparation phases that the "H3 Performance Roadmap" page separates out
+// for SageAttention 2.2.0 (K smoothing, Q/K INT8 quantization, V transpose + FP8
+// quantization; the Sage2 decomposition paragraph and "Phase 4: Dense Sage-Compatible
+// Attention").  All three passes are HBM-bound streams:
 //
 //   stats_q  : per (segment, head, chunk of tokens) FP64 sums of K and max|V| per channel;
 //              in the same launch, per (64-token Q block, head) amax -> FP32 scale(s) ->

@@ -3,7 +3,7 @@
 This module only draws inputs; it holds none of the attention program's arithmetic and
 is the single source of inputs for both the HIP path and the CPU oracle.
 
-Shapes follow the pages' H3 workload ("h3-blackwell-runtime/PERFORMANCE_ROADMAP.md",
+Shapes follow the pages' H3 workload ("H3 Performance Roadmap",
 "Measured GB10 Baseline": 37,810 packed tokens of which 100 are text tokens; the
 Phase 2B report's fixed B=1, H=1, Q=128, KV=192, D=128 shape with three K64 epochs).
 The pages measure real block-24 activations, which are not available; these seeded
