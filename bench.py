@@ -224,6 +224,9 @@ def latency(args, w, torch, B):
     fwd()
     torch.cuda.synchronize()
     ref = out.clone()
+    # the split leaves its partial results in the workspace (and its counters at zero); a
+    # forward that does not split never writes it
+    key_split = ws is not None and bool(ws.any())
 
     def sample_times(launch, n, count):
         """n event intervals around `launch()`, each covering `count` kernel launches (us per launch)."""
@@ -275,7 +278,7 @@ def latency(args, w, torch, B):
         "dtype": "int8 (QK) + fp8 e4m3 (PV), fp32 softmax",
         "data": _data_recipe(w),
         "config": {"workload": w.name, "B": Bn, "H": H, "Lq": Lq, "Lk": Lk, "D": 128, "layout": w.layout,
-                   "launches_per_sample": per, "forward_workspace": ws is not None},
+                   "launches_per_sample": per, "forward_workspace": ws is not None, "key_split": key_split},
         "graph_replay_us": stats(graph),
         "eager_us": stats(eager),
         "single_launch_us": stats(single),

@@ -61,3 +61,4 @@ def test_latency_line_fixed_shape():
     g = d["graph_replay_us"]
     assert g["samples"] == 20 and 0 < g["p10"] <= g["p50"] <= g["p90"] < 1000
     assert d["value"] == g["p50"] and d["vs_baseline"] > 0
+    assert d["config"]["forward_workspace"] is True and d["config"]["key_split"] is False  # 3 epochs: too few
