@@ -23,8 +23,8 @@ time of sattn_fwd the way the pages time their fixed-shape kernel: samples of 20
 back-to-back launches, the per-launch time being a sample's event interval over 20; the
 launches are replayed from a captured HIP graph so that host enqueue time (Python and
 ctypes) does not stretch the interval, with the eager figure beside it.  sattn_fwd gets
-its forward workspace (--no-split withholds it), with which grids small enough for both
-halves of every query tile to own a CU split each tile's keys between two workgroups.  Its
+its forward workspace (--no-split withholds it), with which the query tiles of a short last
+dispatch round split their keys between two workgroups on CUs of their own.  Its
 CPU baseline is the whole oracle on the whole shape, on one host thread and on all of them.
 
 --summarize-trace CSV (with the --steps/--warmup of the profiled run) reads a rocprofv3

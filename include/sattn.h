@@ -169,10 +169,11 @@ SATTN_API sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, satt
  * Phase 2B report's "Exactness" section).  B segments of Lq queries and Lk keys, H heads,
  * D = 128.  sm_scale multiplies q·k (usually 1/sqrt(D)); it must be finite and > 0.
  *
- * `workspace` (optional, 16-byte aligned, fwd_workspace_bytes of sattn_quant_query) lets a
- * problem whose grid leaves most CUs idle split the keys of every 128-query tile between
- * two workgroups: taken when both halves of every tile get a CU of their own (at most 128
- * tiles on a 256-CU device) and the keys span at least 16 epochs of 64.  The second half
+ * `workspace` (optional, 16-byte aligned, fwd_workspace_bytes of sattn_quant_query) lets
+ * the 128-query tiles that would run with CUs left idle split their keys between two
+ * workgroups: the tiles of the last dispatch round (two workgroups per CU; the whole grid
+ * when it is shorter than a round) when the halves of each get a CU of their own (at most
+ * 128 tiles on a 256-CU device), and the keys span at least 16 epochs of 64.  The second half
  * starts from the running max over the first half's keys (computed from their scores), so
  * every E4M3 probability equals the sequential recurrence's, and the two partial results
  * are merged as O = O_1 2^(m_1 - m) + O_2 2^(m_2 - m) (d likewise).  The workspace must

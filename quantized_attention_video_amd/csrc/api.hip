@@ -42,12 +42,15 @@ QuantWs quant_ws(int nseg, int H) {
 
 size_t fwd_ws(int nseg) { return align_up((size_t)nseg * 4) + align_up(((size_t)nseg + 1) * 4); }
 
-// Key split of the dense forward: used when the split grid still gives every workgroup a CU of
-// its own (2 * grid <= compute units; 128 query tiles at most on 256 CUs) and the segment has
-// at least kSplitMinEpochs key epochs.  One workgroup alone on a CU already keeps its SIMDs
-// most of the way busy, so a split that puts two on a CU gains less than the second half's
-// running-max pass costs.  The first half takes kSplitE1Num / kSplitE1Den of the epochs: the
-// second half's pass over the first half's keys costs about 0.4 of a full epoch each.
+// Key split of the dense forward.  Workgroups are dispatched round-robin over the 8 XCDs,
+// two per CU at a time; when the last round of an XCD holds few enough workgroups that the
+// two halves of each get a CU of their own (at most a sixteenth of the XCD's CUs' worth of
+// tiles: 16 on MI355X, 128 over the chip), those tiles are split — all of them when the
+// whole grid is that small.  One workgroup alone on a CU already keeps its SIMDs most of
+// the way busy, so a split that puts two on a CU gains less than the second half's
+// running-max pass costs.  The keys must span at least kSplitMinEpochs epochs.  The first
+// half takes kSplitE1Num / kSplitE1Den of the epochs: the second half's pass over the
+// first half's keys costs about a third of a full epoch per epoch.
 constexpr int64_t kSplitMaxTiles = 128;
 constexpr int kSplitMinEpochs = 16;
 constexpr int kSplitE1Num = 5, kSplitE1Den = 8;
@@ -141,12 +144,11 @@ sattn_status sattn_quant_query(int nseg, int64_t total_q, int64_t total_k, int H
   out->v_bytes = out->k_bytes;
   out->v_scale_bytes = out->k_mean_bytes;
   out->quant_workspace_bytes = quant_ws(nseg, H).total;
-  // the key split needs room for its partials only when the grid could be small enough: a
-  // dense problem has between H * total_q / 128 and H * (total_q / 128 + nseg) query tiles
+  // room for the key split's partials: at most kSplitMaxTiles tiles (the last dispatch
+  // round's, or the whole grid's), and never more than the problem has
   const int64_t qpw = attn_queries_per_wg();
-  const int64_t tiles_lo = (int64_t)H * ((total_q + qpw - 1) / qpw);
   const int64_t tiles_hi = (int64_t)H * (total_q / qpw + nseg);
-  const size_t split = tiles_lo <= kSplitMaxTiles ? split_ws_bytes(std::min(tiles_hi, kSplitMaxTiles)) : 0;
+  const size_t split = split_ws_bytes(std::min(tiles_hi, kSplitMaxTiles));
   out->fwd_workspace_bytes = fwd_ws(nseg) > split ? fwd_ws(nseg) : split;
   return SATTN_OK;
 }
@@ -236,24 +238,29 @@ static sattn_status fwd_common(const sattn_qkv_quant* qkv, int H, int D, float s
 
 static float log2e_scale(float sm_scale) { return (float)((double)sm_scale * 1.4426950408889634); }
 
-// The key split of a dense forward (p.split = 2, grid doubled, the workspace's counters and
-// partials wired in) when the workspace is given and large enough, the keys span at least
-// kSplitMinEpochs epochs and both halves of every tile get a CU of their own; else no split.
-static sattn_status plan_split(AttnParams& p, int64_t& grid, int64_t tiles, int64_t Lk, void* workspace,
-                               size_t workspace_bytes) {
+// The key split of a dense forward (p.split = 2, the split tiles' blocks doubled, the
+// workspace's counters and partials wired in) when the workspace is given and large enough,
+// the keys span at least kSplitMinEpochs epochs and the tiles of the last dispatch round can
+// each have two CUs; else no split.  `grid` = 8 blocks per work index (one per XCD).
+static sattn_status plan_split(AttnParams& p, int64_t& grid, int64_t Lk, void* workspace, size_t workspace_bytes) {
   p.split = 1;
-  if (workspace == nullptr || tiles > kSplitMaxTiles || ceil64(Lk) < kSplitMinEpochs ||
-      workspace_bytes < split_ws_bytes(tiles))
-    return SATTN_OK;
+  if (workspace == nullptr || ceil64(Lk) < kSplitMinEpochs) return SATTN_OK;
   int cus = 0;
   if (cu_count(&cus) != SATTN_OK) return SATTN_EHIP;
-  if (2 * grid > cus) return SATTN_OK;
+  const int64_t per_xcd = grid / 8;            // work items per XCD
+  const int64_t slots = (int64_t)cus / 4;      // two workgroups per CU, cus / 8 CUs per XCD
+  const int64_t own = (int64_t)cus / 16;       // last-round items whose halves own a CU
+  const int64_t last = per_xcd % slots;      // the last round's items (all of them in a short grid)
+  if (last == 0 || last > own) return SATTN_OK;
+  const int64_t tiles = (p.H < 8 ? p.H : 8) * last;  // XCDs with heads x last-round items
+  if (tiles > kSplitMaxTiles || workspace_bytes < split_ws_bytes(tiles)) return SATTN_OK;
   p.split = 2;
+  p.split_from = per_xcd - last;
   p.split_e1 = (int)(ceil64(Lk) * kSplitE1Num / kSplitE1Den);
   p.cnt = static_cast<int32_t*>(workspace);
   p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                     (split_ws_bytes(tiles) - (size_t)tiles * 2 * kSplitHalfBytes));
-  grid *= 2;
+  grid += 8 * last;
   return SATTN_OK;
 }
 
@@ -281,7 +288,7 @@ static sattn_status fwd_dense(const sattn_qkv_quant* qkv, int B, int H, int Lq, 
   const int64_t ntile = ceil64(Lq) * 64 / qpw + (ceil64(Lq) * 64 % qpw != 0);
   int64_t grid = 8 * (int64_t)((H + 7) / 8) * B * ntile;
   if (grid > kMaxGroups256) return SATTN_EUNSUPPORTED;
-  st = plan_split(p, grid, (int64_t)B * H * ntile, Lk, workspace, workspace_bytes);
+  st = plan_split(p, grid, Lk, workspace, workspace_bytes);
   if (st != SATTN_OK) return st;
   return launch_attention(p, grid, false, static_cast<hipStream_t>(stream)) == hipSuccess ? SATTN_OK : SATTN_EHIP;
 }
@@ -419,7 +426,7 @@ sattn_status sattn_fwd_fused(const sattn_qkv_quant* kv, sattn_bf16_in q, const i
   int64_t grid = varlen ? 8 * (int64_t)((H + 7) / 8) * (Lq / qpw + nseg + 1) : 8 * (int64_t)((H + 7) / 8) * nseg * ntile;
   if (grid > kMaxGroups256) return SATTN_EUNSUPPORTED;
   if (!varlen) {  // dense: the key split, as in sattn_fwd
-    st = plan_split(p, grid, (int64_t)nseg * H * ntile, Lk, workspace, workspace_bytes);
+    st = plan_split(p, grid, Lk, workspace, workspace_bytes);
     if (st != SATTN_OK) return st;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);

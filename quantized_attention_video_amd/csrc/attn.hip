@@ -547,6 +547,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   // ---------------------------------------------------------------- work item
   int s, h, half = 0;
   int64_t qt;
+  bool split_tile = false;  // this tile's keys are shared with a second workgroup
+  int64_t split_idx = 0;    // its counter and partials in the workspace
   if constexpr (DUMP) {  // the query tiles of one (segment, head) that hold sampled rows
     s = p.dump.seg;
     h = p.dump.head;
@@ -554,9 +556,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   } else {
   const int xcd = blockIdx.x & 7;
   int64_t kk = blockIdx.x >> 3;
-  if (p.split == 2) {  // the two halves of a tile: neighbours on one XCD
-    half = (int)(kk & 1);
-    kk >>= 1;
+  if (p.split == 2 && kk >= p.split_from) {  // the two halves of a tile: neighbours on one XCD
+    const int64_t j = (kk - p.split_from) >> 1;
+    half = (int)((kk - p.split_from) & 1);
+    kk = p.split_from + j;
+    split_tile = true;
+    split_idx = (p.H < 8 ? p.H : 8) * j + xcd;  // XCDs without a head return below
   }
   const int nh = xcd < p.H ? (p.H - xcd + 7) / 8 : 0;
   if (nh == 0) return;
@@ -588,10 +593,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   const SegInfo ki = seg_info(p.gk, s, 0);
   const int nkb_seg = (int)ceil_blocks(ki.len);
   // key split: half 0 takes epochs [0, e1), half 1 [e1, nkb_seg) (the partial last one too)
-  const int e1 = p.split == 2 ? min(p.split_e1, nkb_seg - 1) : nkb_seg;
+  const int e1 = split_tile ? min(p.split_e1, nkb_seg - 1) : nkb_seg;
   const int e0 = half ? e1 : 0;
   const int nkb = half ? nkb_seg - e1 : e1;
-  const int last_valid = (p.split == 2 && half == 0) ? kBlk : (int)(ki.len - (int64_t)(nkb_seg - 1) * kBlk);
+  const int last_valid = (split_tile && half == 0) ? kBlk : (int)(ki.len - (int64_t)(nkb_seg - 1) * kBlk);
   const int64_t qb = qt * kQBlocksPerWG + (wave >> 1);  // this wave's 64-query block
   const int hq = wave & 1;                              // and which 32 of its queries
   if constexpr (DUMP) {  // no sampled row in this tile (uniform over the workgroup): done
@@ -740,7 +745,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
 
   // ---------------------------------------------------------------- epilogue
   float dtot = xhalf_sum(c.dpart);  // = 448 * d
-  if (p.split == 2) {
+  if (split_tile) {
     // Both halves store m, d and O of their rows; the half that finishes second merges:
     // m = max(m_0, m_1), O = O_0 2^(m_0 - m) + O_1 2^(m_1 - m), d likewise, in that order
     // whichever half merges.  The partials move through device-coherent 16-byte stores and
@@ -749,8 +754,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     // are complete before this workgroup's arrival is counted, and the merging half reads
     // only after it saw the other's count.  Agent-scope fences would write back and
     // invalidate the whole L2 of the XCD at every tile's end instead.
-    const int64_t ntile = (ceil_blocks(p.gq.L) + kQBlocksPerWG - 1) / kQBlocksPerWG;
-    const int64_t tile = ((int64_t)s * p.H + h) * ntile + qt;
+    const int64_t tile = split_idx;
     const __amdgpu_buffer_rsrc_t pair = __builtin_amdgcn_make_buffer_rsrc(
         reinterpret_cast<char*>(p.part) + tile * 2 * kSplitHalfBytes, 0, 2 * kSplitHalfBytes, kBufWord3);
     const int mine = (half * 4 + wave) * (kSplitHalfBytes / 4) + lane * 16;

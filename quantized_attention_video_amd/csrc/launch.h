@@ -71,6 +71,10 @@ struct AttnParams {
   float* part;   // [tile][half][wave][17][lane] float4: partial O (16) and (m, d) of each half
   int32_t* cnt;  // [tile]: finished halves; zero between calls
   int split_e1;  // epochs of the first half: [0, split_e1) and [split_e1, end)
+  // Per-XCD work index from which tiles are split (0: every tile); the split tiles' halves
+  // are the blocks 8 * (split_from + 2 j + half) + xcd, and split tile (j, xcd) uses the
+  // counter and partials at index min(H, 8) j + xcd.
+  int64_t split_from;
 };
 
 // One half of a split tile: per wave and lane, 16 float4 of O accumulators and one (m, d).

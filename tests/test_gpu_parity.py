@@ -817,12 +817,21 @@ def _ntile(Lq):
     return -(-(-(-Lq // 64) * 64) // 128)
 
 
-def _splits(Bn, H, Lq, Lk):
-    """The library's rule: both halves of every tile get a CU of their own (2 * grid <= CUs,
-    128 tiles at most) and the keys span at least 16 epochs."""
-    grid = 8 * -(-H // 8) * Bn * _ntile(Lq)
+def _split_last(Bn, H, Lq, Lk):
+    """The library's rule: the work items of each XCD's last dispatch round (two workgroups
+    per CU, cus/8 CUs per XCD; the whole grid when it is shorter than a round) are split
+    when the halves each get a CU of their own (at most cus/16 of them) and the keys span
+    at least 16 epochs.  Returns the split tiles' count (0: no split)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    return 2 * grid <= cus and Bn * H * _ntile(Lq) <= 128 and -(-Lk // 64) >= 16
+    per_xcd = -(-H // 8) * Bn * _ntile(Lq)
+    last = per_xcd % (cus // 4)
+    if last == 0 or last > cus // 16 or -(-Lk // 64) < 16:
+        return 0
+    return min(H, 8) * last
+
+
+def _splits(Bn, H, Lq, Lk):
+    return _split_last(Bn, H, Lq, Lk) > 0
 
 
 def _counter_bytes(tiles):
@@ -880,7 +889,7 @@ def test_key_split_long_keys(Bn, H, Lq, Lk):
     ws = B.split_workspace(Bn, H, Lq, Lk)
     outs = [B.sattn_fwd(quant, Bn, H, Lq, Lk, 0.09, workspace=ws) for _ in range(20)]
     torch.cuda.synchronize()
-    ncnt = _counter_bytes(Bn * H * _ntile(Lq))
+    ncnt = _counter_bytes(_split_last(Bn, H, Lq, Lk))
     assert not ws[:ncnt].any(), "the split counters must be left at zero"
     assert ws[ncnt:].any(), "the split did not run (no partials in the workspace)"
     out = outs[0]
@@ -899,10 +908,38 @@ def test_key_split_long_keys(Bn, H, Lq, Lk):
     _split_oracle_check(out, q, k, v, 0.09, f"split B={Bn} H={H} Lq={Lq} Lk={Lk}", rows)
 
 
+def test_key_split_of_the_last_round():
+    """B=2, H=16, L=2,049: 17 query tiles per (sequence, head), 544 workgroups, 32 more than
+    fit at once, so each XCD's last round holds 4 tiles: those are split (their halves then
+    run on CUs of their own).  20 calls give identical bits, the counters are left at
+    zero; the output differs from the unsplit one only by the summation order of the split
+    tiles and meets the oracle's tolerance on the sampled rows of every head."""
+    name = "ragged_b2_h16_l2049"
+    c = case(name)
+    inp, quant, w = c["inp"], c["quant"], c["w"]
+    Bn, Lq, H = inp["q"].shape[:3]
+    Lk = inp["k"].shape[1]
+    tiles = _split_last(Bn, H, Lq, Lk)
+    assert tiles == 32
+    ws = B.split_workspace(Bn, H, Lq, Lk)
+    outs = [B.sattn_fwd(quant, Bn, H, Lq, Lk, w.sm_scale, workspace=ws) for _ in range(20)]
+    torch.cuda.synchronize()
+    ncnt = _counter_bytes(tiles)
+    assert not ws[:ncnt].any() and ws[ncnt:].any(), "the last round was not split"
+    out = outs[0]
+    assert all(torch.equal(o, out) for o in outs[1:])
+    assert _close_bf16(out, c["out"])
+    rows, ref = oracle_rows(name)
+    got = out.float().cpu()
+    for si in range(len(O.segments(inp["cu_q"]))):
+        _check_output(got[si].numpy()[rows[si]].astype(np.float64), ref[si], f"{name} last-round split seg {si}")
+
+
 @pytest.mark.parametrize("name", ["dense_h8_l4096", "ragged_b2_h16_l1000"])
 def test_key_split_not_taken_on_full_grids(name):
-    """Grids whose halves would share CUs run unsplit even with a workspace: the same bits as
-    without one."""
+    """Grids of 256 workgroups (32 per XCD, one dispatch round; split, their 64 halves would
+    share the XCD's 32 CUs) run unsplit even with a workspace: the same bits as without
+    one, the workspace untouched."""
     c = case(name)
     inp, quant, w = c["inp"], c["quant"], c["w"]
     Bn, Lq, H = inp["q"].shape[:3]
@@ -931,7 +968,7 @@ def test_key_split_small_shapes(Lq, Lk):
     ws = B.split_workspace(Bn, H, Lq, Lk)
     split = B.sattn_fwd(quant, Bn, H, Lq, Lk, 0.09, workspace=ws)
     torch.cuda.synchronize()
-    ncnt = _counter_bytes(Bn * H * _ntile(Lq))
+    ncnt = _counter_bytes(_split_last(Bn, H, Lq, Lk))
     assert not ws[:ncnt].any() and ws[ncnt:].any()
     assert _close_bf16(split, plain)
     cu_q, cu_k = [0, Lq, 2 * Lq], [0, Lk, 2 * Lk]
@@ -970,6 +1007,6 @@ def test_key_split_replays_from_a_captured_graph():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref)
-        assert not ws[:_counter_bytes(H * 9)].any()
+        assert not ws[:_counter_bytes(_split_last(1, H, L, L))].any()
         B.sattn_fwd(quant, 1, H, L, L, 0.09, workspace=ws)  # eager work between the replays
         torch.cuda.synchronize()
