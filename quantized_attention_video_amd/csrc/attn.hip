@@ -41,10 +41,11 @@
 //  * The O rescale by alpha runs only in the lanes whose row max changed, and not at all
 //    when no row of the wave changed (alpha is then exactly 1, so skipping is
 //    bit-identical).
-//  * Key split (a workspace given, both halves of every tile on a CU of their own): two
-//    workgroups share a tile's keys; the second first takes the running max over the
-//    first half's scores, so every probability word is the sequential recurrence's, and
-//    the one that finishes second merges the other's partial O, m and d.
+//  * Key split (a workspace given; the tiles of a short last dispatch round, whose halves
+//    then run on CUs of their own): two workgroups share a tile's keys; the second first
+//    takes the running max over the first half's scores, so every probability word is
+//    the sequential recurrence's, and the one that finishes second merges the other's
+//    partial O, m and d.
 //  * Work items (segment, head, 128-query tile) are ordered so that consecutive
 //    workgroups dispatched to one XCD (workgroup b runs on XCD b mod 8) take the same
 //    head and neighbouring query tiles, so the CUs of an XCD stream the same K/V tiles
