@@ -1,5 +1,5 @@
 """Host-side pieces of bench.py (no GPU): the CPU baselines on a small workload, the
-traffic-summary lookup, and the refusal of more than one GPU."""
+traffic-summary lookup, the rocprofv3 summarisers, and the refusal of more than one GPU."""
 import os
 import subprocess
 import sys
@@ -59,3 +59,39 @@ def test_percentiles_and_cv():
     assert bench._pct(xs, 0) == 1.0 and bench._pct(xs, 50) == 3.0 and bench._pct(xs, 100) == 5.0
     assert bench._pct(xs, 10) == 1.4
     assert abs(bench._cv([2.0, 4.0]) - 1.0 / 3.0) < 1e-12
+
+
+def test_trace_and_counter_summaries(tmp_path, capsys):
+    """The rocprofv3 summarisers: warm-up and timed launches apart when a kernel ran
+    steps + warmup times; per-dispatch sums of a counter's dimensions, averaged over the
+    timed dispatches."""
+    import csv
+
+    trace = tmp_path / "t_kernel_trace.csv"
+    with open(trace, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        t = 0
+        for i in range(5):  # 2 warm-up + 3 timed launches of one step kernel: 10, 20, 30, 40, 50 us
+            w.writerow(["void sattn::attn_fwd_kernel<false, true>(sattn::AttnParams)", t, t + 10000 * (i + 1)])
+            t += 100000
+        w.writerow(["__amd_rocclr_copyBuffer", t, t + 7000])
+    bench.summarize_trace(str(trace), steps=3, warmup=2)
+    out = capsys.readouterr().out.splitlines()
+    timed = [ln.split() for ln in out if " timed " in ln]
+    warm = [ln.split() for ln in out if " warm-up " in ln]
+    assert len(timed) == 1 and timed[0][-5] == "3" and float(timed[0][-4]) == 40.0  # mean of 30, 40, 50
+    assert len(warm) == 1 and warm[0][-5] == "2" and float(warm[0][-4]) == 15.0
+    assert any("copyBuffer" in ln and " all " in ln and "7.0" in ln for ln in out)
+
+    cnt = tmp_path / "c_counter_collection.csv"
+    with open(cnt, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Counter_Name", "Dispatch_Id", "Counter_Value"])
+        for d in range(3):  # 1 warm-up + 2 timed dispatches, each counter reported in two dimensions
+            for part in (1.0, 2.0):
+                w.writerow(["stats_q_kernel(int)", "FETCH_SIZE", d + 1, part * (d + 1)])
+    bench.summarize_counters([str(cnt)], steps=2, warmup=1)
+    line = capsys.readouterr().out.strip()
+    assert "stats_q_kernel" in line and "FETCH_SIZE" in line and "n=  2" in line
+    assert line.endswith("mean=7.5")  # (3*2 + 3*3) / 2: the two timed dispatches, dimensions summed
