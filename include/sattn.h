@@ -170,13 +170,14 @@ SATTN_API sattn_status sattn_quantize_qkv(sattn_bf16_in q, sattn_bf16_in k, satt
  * D = 128.  sm_scale multiplies q·k (usually 1/sqrt(D)); it must be finite and > 0.
  *
  * `workspace` (optional, 16-byte aligned, fwd_workspace_bytes of sattn_quant_query) lets
- * the 128-query tiles that would run with CUs left idle split their keys between two
- * workgroups: the tiles of the last dispatch round (two workgroups per CU; the whole grid
- * when it is shorter than a round) when the halves of each get a CU of their own (at most
- * 128 tiles on a 256-CU device), and the keys span at least 16 epochs of 64.  The second half
- * starts from the running max over the first half's keys (computed from their scores), so
- * every E4M3 probability equals the sequential recurrence's, and the two partial results
- * are merged as O = O_1 2^(m_1 - m) + O_2 2^(m_2 - m) (d likewise).  The workspace must
+ * the 128-query tiles that would run with CUs left idle split their keys between 2 or 4
+ * workgroups (pieces): the tiles of the last dispatch round (two workgroups per CU; the
+ * whole grid when it is shorter than a round) when the pieces of each get a CU of their own
+ * (at most 128 tiles in 2 pieces or 64 in 4 on a 256-CU device) and the keys span at least
+ * 16 (32) epochs of 64.  Each later piece starts from the running max over the keys before
+ * it (computed from their scores), so every E4M3 probability equals the sequential
+ * recurrence's, and the partial results are merged in piece order as
+ * O = sum_q O_q 2^(m_q - m), m = max_q m_q (d likewise).  The workspace must
  * hold zeros before its first use and its counters are left zeroed by every call; calls
  * sharing one workspace must not overlap.  NULL (or too small) runs without the split.
  * The split changes the FP32 summation order of O and d only.

@@ -43,17 +43,21 @@ QuantWs quant_ws(int nseg, int H) {
 size_t fwd_ws(int nseg) { return align_up((size_t)nseg * 4) + align_up(((size_t)nseg + 1) * 4); }
 
 // Key split of the dense forward.  Workgroups are dispatched round-robin over the 8 XCDs,
-// two per CU at a time; when the last round of an XCD holds few enough workgroups that the
-// two halves of each get a CU of their own (at most a sixteenth of the XCD's CUs' worth of
-// tiles: 16 on MI355X, 128 over the chip), those tiles are split — all of them when the
+// two per CU at a time; when the last round of an XCD holds few enough tiles that each can
+// be shared by 2 or 4 workgroups (pieces) with a CU of their own (at most an eighth, resp. a
+// quarter, of the XCD's CUs' worth of tiles), those tiles are split — all of them when the
 // whole grid is that small.  One workgroup alone on a CU already keeps its SIMDs most of
-// the way busy, so a split that puts two on a CU gains less than the second half's
-// running-max pass costs.  The keys must span at least kSplitMinEpochs epochs.  The first
-// half takes kSplitE1Num / kSplitE1Den of the epochs: the second half's pass over the
-// first half's keys costs about a third of a full epoch per epoch.
-constexpr int64_t kSplitMaxTiles = 128;
+// the way busy, so pieces that share a CU gain less than their running-max passes cost.
+// A piece needs kSplitMinEpochs / 2 epochs of its own on average.  The piece boundaries
+// balance the pieces: piece q runs a pass over the keys before it (QK and the max, about
+// 0.4 of a full epoch per epoch) and then its own epochs, so piece q gets a share of the
+// epochs proportional to 0.6^q.
+constexpr int64_t kSplitMaxTiles = 128;   // 2 pieces: 16 tiles per XCD on 256 CUs
+constexpr int64_t kSplitMaxTiles4 = 64;   // 4 pieces: 8 tiles per XCD
 constexpr int kSplitMinEpochs = 16;
-constexpr int kSplitE1Num = 5, kSplitE1Den = 8;
+// Cumulative shares (per mille) of the epochs before piece q, for 2 and 4 pieces.
+constexpr int kSplitShare2[2] = {0, 625};
+constexpr int kSplitShare4[4] = {0, 460, 735, 901};
 
 // need_q: the Q buffers take part (false for the fused-Q forward and K/V-only quantization).
 bool quant_bufs_ok(const sattn_qkv_quant* b, bool need_q = true) {
@@ -148,7 +152,8 @@ sattn_status sattn_quant_query(int nseg, int64_t total_q, int64_t total_k, int H
   // round's, or the whole grid's), and never more than the problem has
   const int64_t qpw = attn_queries_per_wg();
   const int64_t tiles_hi = (int64_t)H * (total_q / qpw + nseg);
-  const size_t split = split_ws_bytes(std::min(tiles_hi, kSplitMaxTiles));
+  const size_t split = std::max(split_ws_bytes(std::min(tiles_hi, kSplitMaxTiles), 2),
+                                split_ws_bytes(std::min(tiles_hi, kSplitMaxTiles4), 4));
   out->fwd_workspace_bytes = fwd_ws(nseg) > split ? fwd_ws(nseg) : split;
   return SATTN_OK;
 }
@@ -238,10 +243,10 @@ static sattn_status fwd_common(const sattn_qkv_quant* qkv, int H, int D, float s
 
 static float log2e_scale(float sm_scale) { return (float)((double)sm_scale * 1.4426950408889634); }
 
-// The key split of a dense forward (p.split = 2, the split tiles' blocks doubled, the
-// workspace's counters and partials wired in) when the workspace is given and large enough,
-// the keys span at least kSplitMinEpochs epochs and the tiles of the last dispatch round can
-// each have two CUs; else no split.  `grid` = 8 blocks per work index (one per XCD).
+// The key split of a dense forward (p.split = pieces per split tile, their blocks added to
+// the grid, the workspace's counters and partials wired in) when the workspace is given and
+// large enough, the keys span enough epochs and the tiles of the last dispatch round can
+// each have 2 or 4 CUs; else no split.  `grid` = 8 blocks per work index (one per XCD).
 static sattn_status plan_split(AttnParams& p, int64_t& grid, int64_t Lk, void* workspace, size_t workspace_bytes) {
   p.split = 1;
   if (workspace == nullptr || ceil64(Lk) < kSplitMinEpochs) return SATTN_OK;
@@ -249,18 +254,23 @@ static sattn_status plan_split(AttnParams& p, int64_t& grid, int64_t Lk, void* w
   if (cu_count(&cus) != SATTN_OK) return SATTN_EHIP;
   const int64_t per_xcd = grid / 8;            // work items per XCD
   const int64_t slots = (int64_t)cus / 4;      // two workgroups per CU, cus / 8 CUs per XCD
-  const int64_t own = (int64_t)cus / 16;       // last-round items whose halves own a CU
-  const int64_t last = per_xcd % slots;      // the last round's items (all of them in a short grid)
-  if (last == 0 || last > own) return SATTN_OK;
+  const int64_t last = per_xcd % slots;        // the last round's items (all of them in a short grid)
+  if (last == 0) return SATTN_OK;
   const int64_t tiles = (p.H < 8 ? p.H : 8) * last;  // XCDs with heads x last-round items
-  if (tiles > kSplitMaxTiles || workspace_bytes < split_ws_bytes(tiles)) return SATTN_OK;
-  p.split = 2;
+  int np = 0;
+  for (int k = kMaxPieces; k >= 2 && np == 0; k /= 2)
+    if (k * last <= cus / 8 && ceil64(Lk) >= kSplitMinEpochs * k / 2 &&
+        tiles <= (k == 2 ? kSplitMaxTiles : kSplitMaxTiles4) && workspace_bytes >= split_ws_bytes(tiles, k))
+      np = k;
+  if (np == 0) return SATTN_OK;
+  p.split = np;
   p.split_from = per_xcd - last;
-  p.split_e1 = (int)(ceil64(Lk) * kSplitE1Num / kSplitE1Den);
+  for (int q = 0; q < np; ++q)
+    p.split_e[q] = (int)(ceil64(Lk) * (np == 2 ? kSplitShare2[q] : kSplitShare4[q]) / 1000);
   p.cnt = static_cast<int32_t*>(workspace);
   p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                    (split_ws_bytes(tiles) - (size_t)tiles * 2 * kSplitHalfBytes));
-  grid += 8 * last;
+                                    (split_ws_bytes(tiles, np) - (size_t)tiles * np * kSplitPieceBytes));
+  grid += 8 * last * (np - 1);
   return SATTN_OK;
 }
 

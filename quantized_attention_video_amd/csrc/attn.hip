@@ -282,9 +282,9 @@ __device__ __forceinline__ v4f ld_coherent16(__amdgpu_buffer_rsrc_t r, int off) 
   return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherentAgent));
 }
 
-// Key split, second half: the running max over the first np epochs of the segment (the
-// keys of the other half), exactly as the sequential recurrence has it when it reaches the
-// second half: m = max(m, fl32(max_j acc_j * sigma_e)) per epoch.  QK MFMAs and the row max
+// Key split, a later piece: the running max over the first np epochs of the segment (the
+// keys of the earlier pieces), exactly as the sequential recurrence has it when it reaches
+// this piece: m = max(m, fl32(max_j acc_j * sigma_e)) per epoch.  QK MFMAs and the row max
 // only; the K tiles pass through a three-slot ring with two epochs of prefetch.
 __device__ __forceinline__ float prefix_max(const Pipe& c, const uint8_t* kg0, const_f32* ksc0, int np) {
   float m = -INFINITY;
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level addressing in SGPRs
 
   // ---------------------------------------------------------------- work item
-  int s, h, half = 0;
+  int s, h, piece = 0;
   int64_t qt;
   bool split_tile = false;  // this tile's keys are shared with a second workgroup
   int64_t split_idx = 0;    // its counter and partials in the workspace
@@ -557,9 +557,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   } else {
   const int xcd = blockIdx.x & 7;
   int64_t kk = blockIdx.x >> 3;
-  if (p.split == 2 && kk >= p.split_from) {  // the two halves of a tile: neighbours on one XCD
-    const int64_t j = (kk - p.split_from) >> 1;
-    half = (int)((kk - p.split_from) & 1);
+  if (p.split > 1 && kk >= p.split_from) {  // the pieces of a tile: neighbours on one XCD
+    const int64_t j = (kk - p.split_from) / p.split;
+    piece = (int)(kk - p.split_from - j * p.split);
     kk = p.split_from + j;
     split_tile = true;
     split_idx = (p.H < 8 ? p.H : 8) * j + xcd;  // XCDs without a head return below
@@ -593,11 +593,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   const SegInfo qi = seg_info(p.gq, s, p.o_st);
   const SegInfo ki = seg_info(p.gk, s, 0);
   const int nkb_seg = (int)ceil_blocks(ki.len);
-  // key split: half 0 takes epochs [0, e1), half 1 [e1, nkb_seg) (the partial last one too)
-  const int e1 = split_tile ? min(p.split_e1, nkb_seg - 1) : nkb_seg;
-  const int e0 = half ? e1 : 0;
-  const int nkb = half ? nkb_seg - e1 : e1;
-  const int last_valid = (split_tile && half == 0) ? kBlk : (int)(ki.len - (int64_t)(nkb_seg - 1) * kBlk);
+  // key split: piece q takes epochs [e0, e1) (the last piece the partial last one too)
+  const bool last_piece = !split_tile || piece == p.split - 1;
+  const int e0 = piece ? min(p.split_e[piece], nkb_seg - 1) : 0;
+  const int e1 = last_piece ? nkb_seg : max(e0, min(p.split_e[piece + 1], nkb_seg - 1));
+  const int nkb = e1 - e0;
+  const int last_valid = last_piece ? (int)(ki.len - (int64_t)(nkb_seg - 1) * kBlk) : kBlk;
   const int64_t qb = qt * kQBlocksPerWG + (wave >> 1);  // this wave's 64-query block
   const int hq = wave & 1;                              // and which 32 of its queries
   if constexpr (DUMP) {  // no sampled row in this tile (uniform over the workgroup): done
@@ -641,7 +642,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   c.kg = reinterpret_cast<const uint8_t*>(p.k8) + (ktile0 + e0) * kTileBytes;
   c.vg = p.v8 + (ktile0 + e0) * kTileBytes;
   c.ksc = (const_f32*)(p.k_scale + ktile0 + e0);
-  const bool dma_first = half == 0;
+  const bool dma_first = piece == 0;
   if (dma_first) issue_first_tiles(c, nkb);
   const bool fused_q = p.qbf != nullptr;
   uint4 qraw[8];
@@ -693,13 +694,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   // loop and waits on vmcnt before the QK MFMAs there, which would also wait for the tile
   // requests in flight.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  if (half) {  // the second half of a split tile: the running max over the first half's keys
+  if (piece) {  // a later piece of a split tile: the running max over the earlier keys
     if (fused_q) {  // which needs this wave's Q operands first
       barrier();    // the sibling wave's row maximum in LDS
       if (c.active) fused_q_operands(c, qraw, qamax, p, wave);
     }
     c.m = prefix_max(c, reinterpret_cast<const uint8_t*>(p.k8) + ktile0 * kTileBytes,
-                     (const_f32*)(p.k_scale + ktile0), e1);
+                     (const_f32*)(p.k_scale + ktile0), e0);
   }
   if constexpr (KSL) {  // landed by the barrier before the first step
 #pragma unroll
@@ -728,7 +729,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   barrier();  // Q, K(0), the K scales, the Q row maxima and the zeroed V slot visible
   if constexpr (KSL) c.ks_next = nkb > 0 ? g_ks[0] : 0.f;
-  if (fused_q && !half && c.active) fused_q_operands(c, qraw, qamax, p, wave);
+  if (fused_q && !piece && c.active) fused_q_operands(c, qraw, qamax, p, wave);
   if (nkb > 0) {
     qk_tile(acc[0], kslot<0>(), c.qop, lane, 0);
     qk_tile(acc[1], kslot<0>(), c.qop, lane, 1);
@@ -747,55 +748,80 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   // ---------------------------------------------------------------- epilogue
   float dtot = xhalf_sum(c.dpart);  // = 448 * d
   if (split_tile) {
-    // Both halves store m, d and O of their rows; the half that finishes second merges:
-    // m = max(m_0, m_1), O = O_0 2^(m_0 - m) + O_1 2^(m_1 - m), d likewise, in that order
-    // whichever half merges.  The partials move through device-coherent 16-byte stores and
-    // loads, lane-major so that each instruction covers 1 KiB (they bypass the caches that
-    // are not coherent across the XCDs, so the halves may sit on different XCDs); the stores
-    // are complete before this workgroup's arrival is counted, and the merging half reads
-    // only after it saw the other's count.  Agent-scope fences would write back and
-    // invalidate the whole L2 of the XCD at every tile's end instead.
-    const int64_t tile = split_idx;
-    const __amdgpu_buffer_rsrc_t pair = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<char*>(p.part) + tile * 2 * kSplitHalfBytes, 0, 2 * kSplitHalfBytes, kBufWord3);
-    const int mine = (half * 4 + wave) * (kSplitHalfBytes / 4) + lane * 16;
-    const int other = ((1 - half) * 4 + wave) * (kSplitHalfBytes / 4) + lane * 16;
+    // Every piece stores m, d and O of its rows; the piece that finishes last merges them in
+    // piece order whichever piece that is: m = max_q m_q, O = sum_q O_q 2^(m_q - m) (the
+    // first term a product, then one FMA per piece), d likewise.  The partials move through
+    // device-coherent 16-byte stores and loads, lane-major so that each instruction covers
+    // 1 KiB (they bypass the caches that are not coherent across the XCDs, so the pieces may
+    // sit on different XCDs); the stores are complete before this workgroup's arrival is
+    // counted, and the merging piece reads only after it saw every other's count.
+    // Agent-scope fences would write back and invalidate the whole L2 of the XCD at every
+    // tile's end instead.
+    const int np = p.split;
+    const __amdgpu_buffer_rsrc_t tile_ws = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<char*>(p.part) + split_idx * np * kSplitPieceBytes, 0, np * kSplitPieceBytes, kBufWord3);
+    const int lane_off = wave * (kSplitPieceBytes / 4) + lane * 16;
+    const int mine = piece * kSplitPieceBytes + lane_off;
     if (c.active) {  // uniform over the wave
 #pragma unroll
       for (int w = 0; w < 4; ++w)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          st_coherent16(pair, mine + (4 * w + q4) * 1024, c.oacc[w][4 * q4], c.oacc[w][4 * q4 + 1],
+          st_coherent16(tile_ws, mine + (4 * w + q4) * 1024, c.oacc[w][4 * q4], c.oacc[w][4 * q4 + 1],
                         c.oacc[w][4 * q4 + 2], c.oacc[w][4 * q4 + 3]);
-      st_coherent16(pair, mine + 16 * 1024, c.m, dtot, 0.f, 0.f);
+      st_coherent16(tile_ws, mine + 16 * 1024, c.m, dtot, 0.f, 0.f);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partials are stored
     __syncthreads();
-    if (tid == 0) g_split_order = __hip_atomic_fetch_add(p.cnt + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) g_split_order = __hip_atomic_fetch_add(p.cnt + split_idx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (g_split_order == 0) return;  // the other half merges
-    if (tid == 0) __hip_atomic_store(p.cnt + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // zero for the next call
+    if (g_split_order != np - 1) return;  // a later piece merges
+    if (tid == 0) __hip_atomic_store(p.cnt + split_idx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // zero for the next call
     if (!c.active) return;
-    v4f po[17];
+    float mq[kMaxPieces], dq[kMaxPieces];
 #pragma unroll
-    for (int j = 0; j < 17; ++j) po[j] = ld_coherent16(pair, other + j * 1024);
-    const float m0 = half ? po[16][0] : c.m, m1 = half ? c.m : po[16][0];
-    const float m = fmaxf(m0, m1);
-    const float a0 = __builtin_amdgcn_exp2f(m0 - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
-    {
-      const float d0 = half ? po[16][1] : dtot, d1 = half ? dtot : po[16][1];
-      dtot = __builtin_fmaf(d1, a1, d0 * a0);
+    for (int q = 0; q < kMaxPieces; ++q) {
+      mq[q] = -INFINITY;
+      dq[q] = 0.f;
+      if (q < np) {
+        const v4f md = q == piece ? v4f{c.m, dtot, 0.f, 0.f}
+                                  : ld_coherent16(tile_ws, q * kSplitPieceBytes + lane_off + 16 * 1024);
+        mq[q] = md[0];
+        dq[q] = md[1];
+      }
+    }
+    float m = mq[0];
+#pragma unroll
+    for (int q = 1; q < kMaxPieces; ++q) m = fmaxf(m, mq[q]);
+    float aq[kMaxPieces];
+#pragma unroll
+    for (int q = 0; q < kMaxPieces; ++q) aq[q] = __builtin_amdgcn_exp2f(mq[q] - m);  // 0 past np
+    dtot = dq[0] * aq[0];
+#pragma unroll
+    for (int q = 1; q < kMaxPieces; ++q)
+      if (q < np) dtot = __builtin_fmaf(dq[q], aq[q], dtot);
+    float acc_o[4][16];
+#pragma unroll
+    for (int q = 0; q < kMaxPieces; ++q) {
+      if (q >= np) break;
+      v4f po[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        po[j] = q == piece ? v4f{c.oacc[j >> 2][4 * (j & 3)], c.oacc[j >> 2][4 * (j & 3) + 1],
+                                 c.oacc[j >> 2][4 * (j & 3) + 2], c.oacc[j >> 2][4 * (j & 3) + 3]}
+                           : ld_coherent16(tile_ws, q * kSplitPieceBytes + lane_off + j * 1024);
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float x = po[4 * w + (i >> 2)][i & 3];
+          acc_o[w][i] = q == 0 ? x * aq[0] : __builtin_fmaf(x, aq[q], acc_o[w][i]);
+        }
     }
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-        for (int r3 = 0; r3 < 4; ++r3) {
-          const float x = c.oacc[w][4 * q4 + r3], y = po[4 * w + q4][r3];
-          const float x0 = half ? y : x, x1 = half ? x : y;
-          c.oacc[w][4 * q4 + r3] = __builtin_fmaf(x1, a1, x0 * a0);
-        }
+      for (int i = 0; i < 16; ++i) c.oacc[w][i] = acc_o[w][i];
   }
   if (!c.active) return;
   const float inv = dtot > 0.f ? 1.0f / dtot : 0.f;

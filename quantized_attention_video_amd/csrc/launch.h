@@ -44,6 +44,8 @@ struct DumpParams {
   int64_t tile0;  // first query tile of the launch (workgroup b takes tile tile0 + b)
 };
 
+constexpr int kMaxPieces = 4;  // most workgroups one split tile's keys are shared by
+
 struct AttnParams {
   const int8_t* q8;
   const float* q_scale;
@@ -65,24 +67,27 @@ struct AttnParams {
   int q_scale_shift;    // Q scales per 64-token block: 1 << q_scale_shift (1 or 2)
   const uint16_t* qbf;  // BF16 Q view quantized in the kernel (sattn_fwd_fused), else nullptr
   int64_t qb_sb, qb_st, qb_sh;  // its batch, token and head element strides
-  // Key split (dense problems whose grid leaves CUs idle): 2 = each query tile's epochs are
-  // shared by two workgroups, which merge their partial results; 1 = no split.
+  // Key split (dense problems whose grid leaves CUs idle): the epochs of each split tile
+  // are shared by `split` workgroups (pieces), which merge their partial results; 1 = no
+  // split.  Piece q takes epochs [split_e[q], split_e[q + 1]) (split_e[0] = 0, the last
+  // piece runs to the segment's end, the partial last epoch included).
   int split;
-  float* part;   // [tile][half][wave][17][lane] float4: partial O (16) and (m, d) of each half
-  int32_t* cnt;  // [tile]: finished halves; zero between calls
-  int split_e1;  // epochs of the first half: [0, split_e1) and [split_e1, end)
-  // Per-XCD work index from which tiles are split (0: every tile); the split tiles' halves
-  // are the blocks 8 * (split_from + 2 j + half) + xcd, and split tile (j, xcd) uses the
-  // counter and partials at index min(H, 8) j + xcd.
+  int split_e[kMaxPieces];
+  // Per-XCD work index from which tiles are split (0: every tile); the pieces of split tile
+  // j are the blocks 8 * (split_from + split * j + q) + xcd, and the tile uses the counter
+  // and partials at index min(H, 8) j + xcd.
   int64_t split_from;
+  float* part;   // [tile][piece][wave][17][lane] float4: partial O (16) and (m, d) of each piece
+  int32_t* cnt;  // [tile]: finished pieces; zero between calls
 };
 
-// One half of a split tile: per wave and lane, 16 float4 of O accumulators and one (m, d).
-constexpr int kSplitHalfBytes = 4 * 17 * 64 * 16;
-// Bytes of the key-split workspace for `tiles` query tiles (counters, then partials).
-inline size_t split_ws_bytes(int64_t tiles) {
+// One piece of a split tile: per wave and lane, 16 float4 of O accumulators and one (m, d).
+constexpr int kSplitPieceBytes = 4 * 17 * 64 * 16;
+// Bytes of the key-split workspace for `tiles` query tiles of `pieces` pieces each
+// (counters, then partials).
+inline size_t split_ws_bytes(int64_t tiles, int pieces) {
   const size_t cnt = ((size_t)tiles * 4 + 255) / 256 * 256;
-  return cnt + (size_t)tiles * 2 * kSplitHalfBytes;
+  return cnt + (size_t)tiles * pieces * kSplitPieceBytes;
 }
 
 int stats_chunks(int nseg, int H);

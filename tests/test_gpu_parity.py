@@ -817,17 +817,23 @@ def _ntile(Lq):
     return -(-(-(-Lq // 64) * 64) // 128)
 
 
-def _split_last(Bn, H, Lq, Lk):
+def _split_plan(Bn, H, Lq, Lk):
     """The library's rule: the work items of each XCD's last dispatch round (two workgroups
     per CU, cus/8 CUs per XCD; the whole grid when it is shorter than a round) are split
-    when the halves each get a CU of their own (at most cus/16 of them) and the keys span
-    at least 16 epochs.  Returns the split tiles' count (0: no split)."""
+    into k = 4 or 2 pieces when k of them each get a CU of their own and the keys span at
+    least 8 k epochs.  Returns (split tiles, pieces); (0, 1) when nothing is split."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     per_xcd = -(-H // 8) * Bn * _ntile(Lq)
     last = per_xcd % (cus // 4)
-    if last == 0 or last > cus // 16 or -(-Lk // 64) < 16:
-        return 0
-    return min(H, 8) * last
+    tiles = min(H, 8) * last
+    for k, cap in ((4, 64), (2, 128)):
+        if last and k * last <= cus // 8 and -(-Lk // 64) >= 8 * k and tiles <= cap:
+            return tiles, k
+    return 0, 1
+
+
+def _split_last(Bn, H, Lq, Lk):
+    return _split_plan(Bn, H, Lq, Lk)[0]
 
 
 def _splits(Bn, H, Lq, Lk):
@@ -872,17 +878,18 @@ def _split_oracle_check(out, q, k, v, sm_scale, label, rows=None):
         _check_output(got[s][sel[s]], ref[s], f"{label} seg {s}")
 
 
-@pytest.mark.parametrize("Bn,H,Lq,Lk", [(1, 1, 128, 4096), (1, 2, 1000, 2049), (1, 8, 2048, 1024), (2, 1, 200, 37810)])
-def test_key_split_long_keys(Bn, H, Lq, Lk):
-    """sattn_fwd with its forward workspace on a grid small enough that both halves of every
-    query tile get a CU of their own: the tile's keys are split between two workgroups (the
-    second first takes the running max over the first half's keys, so every E4M3 probability
-    is the sequential recurrence's) and the halves merge.  20 calls in a row give identical
-    bits and leave the counters at zero; the result differs from the unsplit forward only by
-    the order of the O and d sums, equals the fused-Q forward's split bit for bit, and meets
-    the oracle's tolerance (5% of the query rows scaled by 8)."""
+@pytest.mark.parametrize("Bn,H,Lq,Lk,pieces", [(1, 1, 128, 4096, 4), (1, 2, 1000, 2049, 4), (1, 8, 2048, 1024, 2),
+                                              (2, 1, 200, 37810, 4), (1, 8, 1024, 1100, 2)])
+def test_key_split_long_keys(Bn, H, Lq, Lk, pieces):
+    """sattn_fwd with its forward workspace on a grid small enough that 2 or 4 pieces of
+    every query tile get a CU of their own: the tile's keys are split between that many
+    workgroups (each later one first takes the running max over the earlier keys, so every
+    E4M3 probability is the sequential recurrence's) and the pieces merge.  20 calls in a
+    row give identical bits and leave the counters at zero; the result differs from the
+    unsplit forward only by the order of the O and d sums, equals the fused-Q forward's
+    split bit for bit, and meets the oracle's tolerance (5% of the query rows scaled by 8)."""
     _need_gpu()
-    assert _splits(Bn, H, Lq, Lk)
+    assert _split_plan(Bn, H, Lq, Lk)[1] == pieces
     q, k, v = _split_inputs(Bn, H, Lq, Lk, seed=Bn * 1000 + H * 100 + Lk, loud_rows=0.05)
     quant = B.sattn_quantize_qkv(q.cuda(), k.cuda(), v.cuda())
     plain = B.sattn_fwd(quant, Bn, H, Lq, Lk, 0.09)
@@ -919,8 +926,8 @@ def test_key_split_of_the_last_round():
     inp, quant, w = c["inp"], c["quant"], c["w"]
     Bn, Lq, H = inp["q"].shape[:3]
     Lk = inp["k"].shape[1]
-    tiles = _split_last(Bn, H, Lq, Lk)
-    assert tiles == 32
+    tiles, pieces = _split_plan(Bn, H, Lq, Lk)
+    assert tiles == 32 and pieces == 4
     ws = B.split_workspace(Bn, H, Lq, Lk)
     outs = [B.sattn_fwd(quant, Bn, H, Lq, Lk, w.sm_scale, workspace=ws) for _ in range(20)]
     torch.cuda.synchronize()
