@@ -866,11 +866,11 @@ def _split_inputs(Bn, H, Lq, Lk, seed, loud_rows=0.0):
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
-def _split_oracle_check(out, q, k, v, sm_scale, label, rows=None):
+def _split_oracle_check(out, q, k, v, sm_scale, label, rows=None, q_rows=64):
     Bn, Lq, H = q.shape[:3]
     Lk = k.shape[1]
     cu_q, cu_k = [Lq * i for i in range(Bn + 1)], [Lk * i for i in range(Bn + 1)]
-    oq = O.quantize(W.packed_float64(q), W.packed_float64(k), W.packed_float64(v), cu_q, cu_k)
+    oq = O.quantize(W.packed_float64(q), W.packed_float64(k), W.packed_float64(v), cu_q, cu_k, q_rows=q_rows)
     sel = {s: (np.arange(Lq) if rows is None else rows) for s in range(Bn)}
     ref = O.attention(oq, sm_scale, rows=sel)
     got = out.float().cpu().numpy().astype(np.float64)
@@ -913,6 +913,30 @@ def test_key_split_long_keys(Bn, H, Lq, Lk, pieces):
     assert torch.equal(fused, out), "fused-Q split differs from the two-pass split"
     rows = None if Lq * Lk <= 2_100_000 else np.unique(np.r_[0:8, Lq - 8:Lq, np.arange(0, Lq, 37)])
     _split_oracle_check(out, q, k, v, 0.09, f"split B={Bn} H={H} Lq={Lq} Lk={Lk}", rows)
+
+
+def test_key_split_with_32_row_q_scales():
+    """The split with one Q scale per 32 query rows (each wave's own scale; the pieces'
+    running-max passes use it too): 4 pieces of one tile, against the unsplit forward and
+    the oracle's 32-row program, and the fused-Q split bit for bit."""
+    _need_gpu()
+    Bn, H, Lq, Lk = 1, 1, 128, 4096
+    assert _split_plan(Bn, H, Lq, Lk)[1] == 4
+    q, k, v = _split_inputs(Bn, H, Lq, Lk, seed=3232, loud_rows=0.05)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    quant = B.sattn_quantize_qkv(qd, kd, vd, q_scale_rows=32)
+    plain = B.sattn_fwd(quant, Bn, H, Lq, Lk, 0.09)
+    ws = B.split_workspace(Bn, H, Lq, Lk)
+    out = B.sattn_fwd(quant, Bn, H, Lq, Lk, 0.09, workspace=ws)
+    kv = B.sattn_quantize_kv(qd, kd, vd, q_scale_rows=32)
+    ws2 = B.split_workspace(Bn, H, Lq, Lk)
+    fused = B.sattn_fwd_fused(kv, qd, 0.09, Lk=Lk, workspace=ws2)
+    torch.cuda.synchronize()
+    ncnt = _counter_bytes(_split_last(Bn, H, Lq, Lk))
+    assert not ws[:ncnt].any() and ws[ncnt:].any()
+    assert torch.equal(fused, out)
+    assert _close_bf16(out, plain)
+    _split_oracle_check(out, q, k, v, 0.09, "split, 32-row Q scales", q_rows=32)
 
 
 def test_key_split_of_the_last_round():
